@@ -1,0 +1,72 @@
+"""Build step: compiles the HIP sources into the in-tree shared library.
+
+One translation unit (csrc/adamw_sr.hip, which includes csrc/device.hpp and
+include/adamw_sr.h) -> libadamw_sr.so, for gfx950 only. Flags that matter
+for the arithmetic:
+  -ffp-contract=off                          no fused multiply-adds (the
+                                             sources also say so by pragma)
+  -fhip-fp32-correctly-rounded-divide-sqrt   '/' and sqrt correctly rounded
+  no -ffast-math, no denormal flushing       subnormals kept
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                             no packed f32 instructions
+The library is written to a temporary name and renamed into place, so a
+process that has the old library mapped is not disturbed.
+"""
+
+import os
+import shutil
+import subprocess
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+SOURCES = [os.path.join(PKG_DIR, "csrc", "adamw_sr.hip")]
+DEPENDS = SOURCES + [os.path.join(PKG_DIR, "csrc", "device.hpp"),
+                     os.path.join(ROOT, "include", "adamw_sr.h")]
+LIB_NAME = "libadamw_sr.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wextra", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc():
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found (ROCm is required to build libadamw_sr.so)")
+    return path
+
+
+def build(out_path=LIB_PATH, extra_flags=(), verbose=False):
+    """Compile the library. Always compiles (no up-to-date check)."""
+    fd, tmp = tempfile.mkstemp(prefix=".libadamw_sr.", suffix=".so.tmp",
+                               dir=os.path.dirname(out_path))
+    os.close(fd)
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
+           *SOURCES, "-o", tmp]
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        noise = "packed-fp32-ops"  # the host pass does not know the feature
+        msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+        if verbose and msgs:
+            print("\n".join(msgs))
+        os.replace(tmp, out_path)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return out_path
+
+
+def is_built():
+    return os.path.exists(LIB_PATH)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

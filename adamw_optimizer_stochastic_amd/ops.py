@@ -1,0 +1,141 @@
+"""Tensor-level entry points over the C ABI (torch supplies memory and streams).
+
+Each function checks devices, dtypes, sizes and contiguity, then calls the
+C entry point of the same name (without the ``asr_`` prefix) on the current
+HIP stream of the tensors' device. All arithmetic runs in the library's
+kernels; there is no CPU path.
+"""
+
+import torch
+
+from . import _abi
+from ._abi import ASR_F32, ASR_BF16, ASR_ROUND_SR, ASR_ROUND_RN, AsrError  # noqa: F401
+
+_DTYPE_CODE = {torch.float32: ASR_F32, torch.bfloat16: ASR_BF16}
+ROUNDING_CODE = {"sr": ASR_ROUND_SR, "rn": ASR_ROUND_RN}
+
+
+def _require_gpu(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(n_tensors):
+    return _abi.asr_adamw_workspace_bytes(n_tensors)
+
+
+def make_workspace(n_tensors, device):
+    """A device buffer big enough for a list of n_tensors."""
+    return torch.empty(max(workspace_bytes(n_tensors), 1), dtype=torch.uint8, device=device)
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1, beta2,
+               eps, weight_decay, step, seed, rounding="sr", workspace=None):
+    """One fused AdamW step over lists of tensors on one device (in place).
+
+    params: f32 or bf16; grads: f32 or bf16, same numel as their param;
+    exp_avgs / exp_avg_sqs: f32; base_indices: global position of element 0
+    of each tensor. ``rounding`` ("sr" | "rn") applies to bf16 params.
+    """
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == len(base_indices) == n):
+        raise ValueError("all lists must have the same length")
+    if rounding not in ROUNDING_CODE:
+        raise ValueError("rounding must be 'sr' or 'rn'")
+    if n == 0:
+        return
+    device = params[0].device
+    descs = []
+    for i, (p, g, m, v, b) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs, base_indices)):
+        for t, name in ((p, "param"), (g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")):
+            _require_gpu(t, f"{name}[{i}]")
+            if t.device != device:
+                raise ValueError("all tensors must be on one device")
+        if p.dtype not in _DTYPE_CODE or g.dtype not in _DTYPE_CODE:
+            raise TypeError(f"tensor {i}: params and grads must be float32 or bfloat16")
+        if m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError(f"tensor {i}: optimizer states must be float32")
+        if not (p.numel() == g.numel() == m.numel() == v.numel()):
+            raise ValueError(f"tensor {i}: param, grad and states differ in size")
+        descs.append(_abi.AsrTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
+                                    p.numel(), int(b) & 0xFFFFFFFFFFFFFFFF,
+                                    _DTYPE_CODE[p.dtype], _DTYPE_CODE[g.dtype]))
+    need = workspace_bytes(n)
+    if workspace is None:
+        workspace = make_workspace(n, device)
+    if workspace.device != device or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be on {device} and hold {need} bytes")
+    with torch.cuda.device(device):
+        _abi.asr_adamw_step(descs, float(lr), float(beta1), float(beta2), float(eps),
+                            float(weight_decay), int(step), int(seed), ROUNDING_CODE[rounding],
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            _stream(device))
+
+
+def philox_4x32_fill(n_counters, counter_base, seed, step, counter_upper=0, *, out=None,
+                     device="cuda"):
+    """Words of n_counters Philox4x32-10 calls as an int32 tensor of 4*n_counters
+    (reinterpret as uint32)."""
+    if out is None:
+        out = torch.empty(4 * n_counters, dtype=torch.int32, device=device)
+    _require_gpu(out, "out")
+    if out.dtype != torch.int32 or out.numel() != 4 * n_counters:
+        raise ValueError("out must be int32 with 4*n_counters elements")
+    with torch.cuda.device(out.device):
+        _abi.asr_philox_4x32_fill(out.data_ptr(), n_counters, int(counter_base) % (1 << 64),
+                                  int(counter_upper) % (1 << 64), int(seed), int(step),
+                                  _stream(out.device))
+    return out
+
+
+def _convert_args(x, out):
+    _require_gpu(x, "x")
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _require_gpu(out, "out")
+    if out.dtype != torch.bfloat16 or out.numel() != x.numel() or out.device != x.device:
+        raise ValueError("out must be bfloat16 with x's size, on x's device")
+    return out
+
+
+def cvt_f32_bf16_sr(x, seed, step, base_index=0, *, out=None):
+    """Stochastic rounding f32 -> bf16 (element i at position base_index + i)."""
+    out = _convert_args(x, out)
+    with torch.cuda.device(x.device):
+        _abi.asr_cvt_f32_bf16_sr(x.data_ptr(), out.data_ptr(), x.numel(), int(seed), int(step),
+                                 int(base_index) % (1 << 64), _stream(x.device))
+    return out
+
+
+def cvt_f32_bf16_rn(x, *, out=None):
+    """Round-to-nearest-even f32 -> bf16."""
+    out = _convert_args(x, out)
+    with torch.cuda.device(x.device):
+        _abi.asr_cvt_f32_bf16_rn(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device))
+    return out
+
+
+def f32_sqrt_div(a, b):
+    """(sqrt(a), a / b) as the AdamW kernel evaluates them (test support)."""
+    for t, name in ((a, "a"), (b, "b")):
+        _require_gpu(t, name)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if a.numel() != b.numel() or a.device != b.device:
+        raise ValueError("a and b must match in size and device")
+    s = torch.empty_like(a)
+    d = torch.empty_like(a)
+    with torch.cuda.device(a.device):
+        _abi.asr_f32_sqrt_div(a.data_ptr(), b.data_ptr(), s.data_ptr(), d.data_ptr(), a.numel(),
+                              _stream(a.device))
+    return s, d

@@ -1,0 +1,127 @@
+"""AdamWSR: a torch.optim.Optimizer over the fused AdamW-SR kernels.
+
+From the "adamw-sr" page (Usage section): a drop-in for torch.optim.AdamW
+taking lr, weight_decay and seed; optimizer states are float32; parameters
+and gradients may be f32 or bf16; stochastic rounding is on by default for
+bf16 parameters. The Method section indexes the randomness by each
+element's global parameter position; reading: the position of a tensor's
+first element is the running total of numel over all parameters of the
+optimizer, in param_groups order and then parameter order, fixed when the
+parameter is added (later groups are appended after it).
+
+Unsupported AdamW options raise NotImplementedError rather than silently
+computing something else.
+"""
+
+import torch
+
+from . import ops
+
+
+class AdamWSR(torch.optim.Optimizer):
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=1e-2,
+                 *, seed=0, rounding="sr", amsgrad=False, maximize=False, foreach=None,
+                 capturable=False, differentiable=False, fused=None):
+        if amsgrad:
+            raise NotImplementedError("AdamWSR: amsgrad is not supported")
+        if maximize:
+            raise NotImplementedError("AdamWSR: maximize is not supported")
+        if capturable or differentiable:
+            raise NotImplementedError("AdamWSR: capturable/differentiable are not supported")
+        if foreach or fused:
+            raise NotImplementedError("AdamWSR is always one fused multi-tensor kernel; "
+                                      "foreach/fused flags are not accepted")
+        if isinstance(lr, torch.Tensor):
+            raise NotImplementedError("AdamWSR: tensor lr is not supported")
+        if not 0.0 <= lr:
+            raise ValueError(f"Invalid learning rate: {lr}")
+        if not 0.0 <= eps:
+            raise ValueError(f"Invalid epsilon value: {eps}")
+        if not (0.0 <= betas[0] < 1.0 and 0.0 <= betas[1] < 1.0):
+            raise ValueError(f"Invalid beta parameters: {betas}")
+        if not 0.0 <= weight_decay:
+            raise ValueError(f"Invalid weight_decay value: {weight_decay}")
+        if rounding not in ("sr", "rn"):
+            raise ValueError("rounding must be 'sr' or 'rn'")
+        if not (isinstance(seed, int) and 0 <= seed < (1 << 32)):
+            raise ValueError("seed must be an integer in [0, 2**32)")
+        self.seed = seed
+        self._base_index = {}
+        self._next_index = 0
+        self._workspaces = {}
+        defaults = dict(lr=lr, betas=tuple(betas), eps=eps, weight_decay=weight_decay,
+                        rounding=rounding)
+        super().__init__(params, defaults)
+
+    def add_param_group(self, param_group):
+        super().add_param_group(param_group)
+        for p in self.param_groups[-1]["params"]:
+            if p in self._base_index:
+                continue
+            if p.is_sparse or p.is_complex() or p.dtype not in (torch.float32, torch.bfloat16):
+                raise NotImplementedError(
+                    f"AdamWSR supports dense float32/bfloat16 params (got {p.dtype})")
+            self._base_index[p] = self._next_index
+            self._next_index += p.numel()
+
+    def base_index(self, p):
+        """Global position of element 0 of parameter p."""
+        return self._base_index[p]
+
+    def _workspace(self, device, n):
+        ws = self._workspaces.get(device)
+        if ws is None or ws.numel() < ops.workspace_bytes(n):
+            ws = ops.make_workspace(max(n, 64), device)
+            self._workspaces[device] = ws
+        return ws
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for group in self.param_groups:
+            beta1, beta2 = group["betas"]
+            batches = {}  # (device, step) -> lists
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                if p.grad.is_sparse:
+                    raise NotImplementedError("AdamWSR does not support sparse gradients")
+                if not p.is_contiguous() or not p.grad.is_contiguous():
+                    raise NotImplementedError("AdamWSR needs contiguous params and grads")
+                state = self.state[p]
+                if len(state) == 0:
+                    state["step"] = torch.tensor(0.0, dtype=torch.float32)
+                    state["exp_avg"] = torch.zeros_like(p, dtype=torch.float32,
+                                                        memory_format=torch.contiguous_format)
+                    state["exp_avg_sq"] = torch.zeros_like(p, dtype=torch.float32,
+                                                           memory_format=torch.contiguous_format)
+                state["step"] += 1
+                t = int(state["step"].item())
+                key = (p.device, t)
+                b = batches.setdefault(key, ([], [], [], [], []))
+                b[0].append(p)
+                b[1].append(p.grad)
+                b[2].append(state["exp_avg"])
+                b[3].append(state["exp_avg_sq"])
+                b[4].append(self._base_index[p])
+            for (device, t), (ps, gs, ms, vs, bases) in batches.items():
+                ops.adamw_step(ps, gs, ms, vs, bases, lr=group["lr"], beta1=beta1, beta2=beta2,
+                               eps=group["eps"], weight_decay=group["weight_decay"], step=t,
+                               seed=self.seed, rounding=group["rounding"],
+                               workspace=self._workspace(device, len(ps)))
+        return loss
+
+    def state_dict(self):
+        sd = super().state_dict()
+        sd["adamw_sr"] = {"seed": self.seed}
+        return sd
+
+    def load_state_dict(self, state_dict):
+        extra = state_dict.get("adamw_sr")
+        state_dict = {k: v for k, v in state_dict.items() if k != "adamw_sr"}
+        super().load_state_dict(state_dict)
+        if extra is not None:
+            self.seed = int(extra["seed"])

@@ -1,0 +1,126 @@
+"""Seeded synthetic workloads (shapes and input generators only).
+
+Nothing here computes any part of the method: these functions only draw
+inputs, which the tests and the benchmark feed byte-identically to the GPU
+path and to the oracle. Draws are N(0, std) (std = standard deviation);
+bf16 inputs are f32 draws cast by torch's round-to-nearest-even cast.
+
+Workloads (sizes as used by the tests and the benchmark):
+  * small:   one bf16 tensor of 65,536 elements, params ~N(0, 0.02), grads
+             ~N(0, 1e-3) drawn afresh each step, m = v = 0, 10 steps;
+  * subulp:  1,048,576 bf16 params equal to 1.0, grad = w - 1.5 (f32),
+             lr 1e-4, wd 0, 6,000 steps;
+  * f32:     16,777,216 f32 params ~N(0, 0.02), f32 grads ~N(0, 1e-2) each
+             step, 100 steps;
+  * convert: 2**30 f32 values ~N(0, 1) with 0.1% of positions replaced by
+             a cycle of +-Inf, NaNs with various payloads and +-FLT_MAX;
+  * shards:  268,435,456 bf16 params ~N(0, 0.02), bf16 grads ~N(0, 1e-3);
+  * llama3_8b: the parameter list of a Llama-3-8B-shaped model (291
+             tensors, 8,030,261,248 elements), bf16 matrices ~N(0, 0.02),
+             RMSNorm weights 1.0, bf16 grads ~N(0, 1e-3), f32 m = v = 0.
+"""
+
+import numpy as np
+import torch
+
+# ---------------------------------------------------------------- shapes
+LLAMA3_8B = dict(hidden=4096, ffn=14336, layers=32, q_heads=32, kv_heads=8, head_dim=128,
+                 vocab=128256)
+
+
+def llama3_8b_shapes(cfg=LLAMA3_8B):
+    """(name, shape) of every parameter, in module registration order."""
+    h, f, hd = cfg["hidden"], cfg["ffn"], cfg["head_dim"]
+    q, kv = cfg["q_heads"] * hd, cfg["kv_heads"] * hd
+    out = [("embed_tokens", (cfg["vocab"], h))]
+    for i in range(cfg["layers"]):
+        pre = f"layers.{i}."
+        out += [(pre + "self_attn.q_proj", (q, h)), (pre + "self_attn.k_proj", (kv, h)),
+                (pre + "self_attn.v_proj", (kv, h)), (pre + "self_attn.o_proj", (h, q)),
+                (pre + "mlp.gate_proj", (f, h)), (pre + "mlp.up_proj", (f, h)),
+                (pre + "mlp.down_proj", (h, f)),
+                (pre + "input_layernorm", (h,)), (pre + "post_attention_layernorm", (h,))]
+    out += [("norm", (h,)), ("lm_head", (cfg["vocab"], h))]
+    return out
+
+
+def numel(shape):
+    n = 1
+    for s in shape:
+        n *= int(s)
+    return n
+
+
+# ------------------------------------------------------------ host draws
+CFG_SMALL, CFG_SUBULP, CFG_F32, CFG_CONVERT, CFG_SHARDS, CFG_LLAMA = 1, 2, 3, 4, 5, 6
+
+
+def host_rng(cfg_id, seed=0, step=0):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg_id, seed, step])))
+
+
+def normal_f32(rng, n, std):
+    return (rng.standard_normal(n) * std).astype(np.float32)
+
+
+def f32_to_bf16_bits(x):
+    """float32 numpy array -> uint16 bf16 patterns by torch's RNE cast."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_tensor(h, device):
+    return torch.from_numpy(np.ascontiguousarray(h, dtype=np.uint16).view(np.int16)).view(
+        torch.bfloat16).to(device)
+
+
+def tensor_to_bf16_bits(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+SPECIAL_F32_BITS = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7F800001,
+                             0x7FFFFFFF, 0xFFFFFFFF, 0xFF800001, 0x7F7FFFFF, 0xFF7FFFFF],
+                            dtype=np.uint32)
+
+
+def inject_specials(x, fraction, rng):
+    """Replace round(fraction * n) distinct positions of float32 array x (in
+    place) by a cycle over SPECIAL_F32_BITS. Returns the positions."""
+    n = x.size
+    k = int(round(fraction * n))
+    pos = np.sort(rng.choice(n, size=k, replace=False))
+    x.view(np.uint32)[pos] = SPECIAL_F32_BITS[np.arange(k) % SPECIAL_F32_BITS.size]
+    return pos
+
+
+# ---------------------------------------------------------- device draws
+def device_generator(device, cfg_id, seed=0, step=0):
+    g = torch.Generator(device=device)
+    g.manual_seed((cfg_id << 40) ^ (seed << 20) ^ step)
+    return g
+
+
+def device_normal(n, std, gen, device, dtype):
+    x = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+    x.mul_(std)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+def llama3_8b_state(device, seed=0, param_std=0.02, grad_std=1e-3, cfg=LLAMA3_8B):
+    """Allocates the full list on `device`: list of dicts with name, param,
+    grad, exp_avg, exp_avg_sq, base_index (running total of numel)."""
+    gen = device_generator(device, CFG_LLAMA, seed)
+    out, base = [], 0
+    for name, shape in llama3_8b_shapes(cfg):
+        n = numel(shape)
+        if len(shape) == 1:
+            p = torch.ones(n, dtype=torch.bfloat16, device=device)
+        else:
+            p = device_normal(n, param_std, gen, device, torch.bfloat16)
+        g = device_normal(n, grad_std, gen, device, torch.bfloat16)
+        out.append(dict(name=name, param=p, grad=g,
+                        exp_avg=torch.zeros(n, dtype=torch.float32, device=device),
+                        exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=device),
+                        base_index=base))
+        base += n
+    return out

@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark: one fused AdamW-SR step over the Llama-3-8B-shaped parameter
+list (291 tensors, 8,030,261,248 bf16 params, bf16 grads, f32 m/v) on one
+MI355X, through the C ABI.
+
+Prints one JSON line: params updated per second (whole step, inputs resident
+in HBM), the dominant kernel's achieved HBM bandwidth against the 8 TB/s
+peak (algorithmic bytes: 22 per element), and the CPU oracle timed on a
+bounded sample of the same workload on the host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|shards|convert]
+    python bench.py --copy-probe      # plain copy of known size (counter scaling)
+"""
+
+import argparse
+import hashlib
+import json
+import multiprocessing
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "params updated/sec and achieved HBM GB/s (% of peak), fused AdamW-SR, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f)
+                  for f in ("adamw_sr.hip", "device.hpp")]
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------- CPU baseline
+def _oracle_shard(args):
+    import numpy as np
+    import oracle
+    from adamw_optimizer_stochastic_amd import workloads as wl
+    shard, n = args
+    rng = wl.host_rng(wl.CFG_LLAMA, 1000 + shard, 0)
+    p = wl.f32_to_bf16_bits(wl.normal_f32(rng, n, 0.02))
+    g = wl.f32_to_bf16_bits(wl.normal_f32(rng, n, 1e-3))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    t0 = time.perf_counter()
+    oracle.step_tensor(p, g, m, v, param_dtype=oracle.BF16, grad_dtype=oracle.BF16,
+                       base_index=shard * n, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                       weight_decay=0.01, step=2, seed=0)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(per_core=1 << 21):
+    """The oracle (numpy, unmodified) on `cores` shards of `per_core` bf16
+    elements each, one process per core, before the GPU is touched (the pool
+    forks a process that has not initialised the GPU)."""
+    cores = max(1, min(16, os.cpu_count() or 1))
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_shard, [(k, per_core) for k in range(cores)])
+    wall = time.perf_counter() - t0
+    n = cores * per_core
+    return {"value": n / wall, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} bf16 params ({cores} shards of {per_core}) of the same workload, "
+                      f"one AdamW-SR step, numpy oracle; wall {wall:.2f} s"}
+
+
+# ------------------------------------------------------------- GPU legs
+def traffic_from_profile(workload, n_elems):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILE_DIR, f"adamw_sr_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != source_hash() or d.get("n_elems") != n_elems:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def run_adamw(args, torch, ops, wl):
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.workload == "llama3_8b":
+        state = wl.llama3_8b_state(dev, seed=0)
+        cfg_name = "llama3_8b_param_list"
+    else:  # shards: one 268,435,456-element tensor
+        n = 268435456
+        gen = wl.device_generator(dev, wl.CFG_SHARDS, 0)
+        state = [dict(name="w", param=wl.device_normal(n, 0.02, gen, dev, torch.bfloat16),
+                      grad=wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16),
+                      exp_avg=torch.zeros(n, dtype=torch.float32, device=dev),
+                      exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=dev),
+                      base_index=0)]
+        cfg_name = "single_tensor_268M"
+    n_elems = sum(t["param"].numel() for t in state)
+    lists = ([t["param"] for t in state], [t["grad"] for t in state],
+             [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
+             [t["base_index"] for t in state])
+    ws = ops.make_workspace(len(state), dev)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0,
+              rounding="sr", workspace=ws)
+    torch.cuda.synchronize()
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        ops.adamw_step(*lists, step=step, **hp)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step += 1
+        events[k][0].record(stream)
+        ops.adamw_step(*lists, step=step, **hp)
+        events[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in events]
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = sum(launch_ms) / len(launch_ms)
+    bytes_per_launch = 22 * n_elems
+    achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(args.workload, n_elems)
+    return {
+        "metric": METRIC, "value": n_elems / (ms_per_step * 1e-3), "unit": "params/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg_name, "n_tensors": len(state), "params": n_elems,
+                   "param_dtype": "bf16", "grad_dtype": "bf16", "state_dtype": "f32",
+                   "rounding": "sr", "algorithmic_bytes_per_param": 22,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "adamw_sr_multi_tensor<BF16,BF16,SR>",
+                     "kernel_ms_avg": kernel_ms,
+                     "timing": "HIP events on the launch stream around each step call "
+                               "(includes its metadata upload launches)"},
+    }
+
+
+def run_convert(args, torch, ops, wl):
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    n = 1 << 30
+    gen = wl.device_generator(dev, wl.CFG_CONVERT, 0)
+    x = wl.device_normal(n, 1.0, gen, dev, torch.float32)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        ops.cvt_f32_bf16_sr(x, 7, 0, 0, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        events[k][0].record(stream)
+        ops.cvt_f32_bf16_sr(x, 7, 0, 0, out=out)
+        events[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    achieved = 6 * n / (kernel_ms * 1e-3) / 1e9
+    return {"metric": "elements converted/sec, cvt_f32_bf16_sr", "value": n / (wall / args.steps),
+            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+            "config": {"workload": "cvt_f32_bf16_sr_2^30"},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel_ms_avg": kernel_ms}}
+
+
+def run_copy_probe(args, torch):
+    """A plain device copy of 8 GiB (torch's copy kernel), for scaling the
+    FETCH_SIZE/WRITE_SIZE counters: it moves exactly 8 GiB each way."""
+    dev = torch.device("cuda", 0)
+    n = 8 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    return {"probe": "copy", "bytes_each_way": n, "ms": ms, "GBps": 2 * n / (ms * 1e-3) / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "shards", "convert"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the optimizer step has no cross-GPU exchange "
+              "(each rank would run the same kernel on its own shard with its own "
+              "base_index), and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.copy_probe and args.workload == "llama3_8b":
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    import torch
+    from adamw_optimizer_stochastic_amd import ops
+    from adamw_optimizer_stochastic_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        print(json.dumps(run_copy_probe(args, torch)))
+        return
+    print(f"[bench] {args.workload}: warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    if args.workload == "convert":
+        res = run_convert(args, torch, ops, wl)
+    else:
+        res = run_adamw(args, torch, ops, wl)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * adamw_sr.h -- C ABI of the fused AdamW step with stochastic-rounding bf16
+ * write-back, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   - "adamw-sr" (kernels hub page), intro, Usage, Method, Correctness:
+ *     a decoupled-weight-decay Adam step with float32 moment states, f32 or
+ *     bf16 parameters and gradients, bf16 parameters written back by
+ *     unbiased stochastic rounding with no fp32 master copy, randomness from
+ *     counter-based Philox keyed by (seed, step) and indexed by each
+ *     element's global parameter position, so whole and sharded updates
+ *     agree bit for bit when each shard passes its own base_index;
+ *   - "Add stochastic rounding and philox RNG helpers" (FlyDSL pull request),
+ *     Primitives: philox_4x32(counter, key) -> four 32-bit words, and
+ *     stochastic rounding f32 -> bf16 by adding 16 random bits to the 16
+ *     dropped mantissa bits and truncating; discussion: stochastic rounding
+ *     as a rounding mode of the narrowing conversion.
+ *
+ * Conventions shared by every entry point:
+ *   - All device pointers are HIP device (or managed) memory owned by the
+ *     caller; the library allocates no device memory and keeps no generator
+ *     state (the generator is counter-based).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream of
+ *     the current device). The current device must be the stream's device.
+ *     Work is enqueued asynchronously; no call synchronizes the host. A
+ *     device-side fault surfaces at the caller's next synchronization.
+ *   - Every call returns an asr_status. On a non-zero status nothing was
+ *     enqueued (argument errors are found before any launch) unless the
+ *     status is ASR_EHIP, and asr_last_error() describes the problem.
+ *   - Element counts are int64_t; global positions are uint64_t and wrap
+ *     modulo 2**64.
+ *
+ * Random-bit contract (the "stream"), used by asr_adamw_step and
+ * asr_cvt_f32_bf16_sr: element i of a tensor whose first element sits at
+ * global position base_index has position p = base_index + i (64-bit).
+ * Its 16 random bits are the low 16 bits of word (p & 3) of
+ * Philox4x32-10(counter = (lo32(p >> 2), hi32(p >> 2), 0, 0),
+ *              key     = (seed, step)).
+ * Philox4x32-10 is the published generator of Salmon et al. (SC 2011):
+ * multipliers 0xD2511F53 (word 0) and 0xCD9E8D57 (word 2), key bumps
+ * 0x9E3779B9 and 0xBB67AE85, 10 rounds.
+ *
+ * Rounding rules (bit patterns u of f32, results are bf16 patterns):
+ *   SR: NaN -> (u >> 16) | 0x0040 (stays NaN, sign and top payload kept);
+ *       otherwise (u + r16) >> 16 in 32-bit arithmetic.
+ *   RN: NaN as above; otherwise round to nearest, ties to even.
+ */
+#ifndef ADAMW_SR_H
+#define ADAMW_SR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum asr_status {
+  ASR_OK = 0,
+  ASR_EINVAL = 1,     /* an argument value is out of its documented range      */
+  ASR_EDTYPE = 2,     /* a dtype code is neither ASR_F32 nor ASR_BF16          */
+  ASR_EALIGN = 3,     /* a pointer is not aligned to its element size          */
+  ASR_EWORKSPACE = 4, /* workspace NULL, smaller than required, or misaligned  */
+  ASR_EHIP = 5        /* the HIP runtime reported an error (see last_error)    */
+} asr_status;
+
+enum { ASR_F32 = 0, ASR_BF16 = 1 };
+enum { ASR_ROUND_SR = 0, ASR_ROUND_RN = 1 };
+
+/* One tensor of the optimizer's list, flattened and contiguous. */
+typedef struct asr_tensor {
+  void* param;          /* numel elements of param_dtype, updated in place   */
+  const void* grad;     /* numel elements of grad_dtype, read only           */
+  float* exp_avg;       /* numel f32: first moment m, updated in place       */
+  float* exp_avg_sq;    /* numel f32: second moment v, updated in place      */
+  int64_t numel;        /* >= 0; a tensor with numel 0 is skipped            */
+  uint64_t base_index;  /* global position of element 0 (random-bit stream)  */
+  int32_t param_dtype;  /* ASR_F32 | ASR_BF16                                */
+  int32_t grad_dtype;   /* ASR_F32 | ASR_BF16                                */
+} asr_tensor;
+
+/* Bytes of device workspace asr_adamw_step needs for a list of n_tensors
+ * (0 for n_tensors <= 0). The workspace holds the list's metadata table. */
+size_t asr_adamw_workspace_bytes(int32_t n_tensors);
+
+/*
+ * One AdamW step over a list of tensors, in one pass over memory.
+ * ("adamw-sr" page: intro, Usage, Method, Correctness.)
+ *
+ * For every element, in binary32, each operation rounded to nearest even
+ * and never fused into a multiply-add:
+ *     m   = b1*m + omb1*g
+ *     v   = b2*v + omb2*(g*g)
+ *     p   = p*decay - step_size * (m / (sqrt(v)*inv_bc2_sqrt + eps32))
+ * where g and p are the gradient and parameter upcast exactly to f32, and the
+ * constants are formed once per call in binary64 (bc1 = 1 - beta1**step,
+ * bc2 = 1 - beta2**step by binary powering) and rounded to binary32:
+ *     decay = 1 - lr*weight_decay, b1 = beta1, omb1 = 1 - beta1, b2 = beta2,
+ *     omb2 = 1 - beta2, step_size = lr/bc1, inv_bc2_sqrt = 1/sqrt(bc2),
+ *     eps32 = eps    (asr_adamw_host_scalars returns them).
+ * m and v are stored as f32. An f32 parameter is stored as computed; a bf16
+ * parameter is rounded by SR (rounding = ASR_ROUND_SR; key (seed, step),
+ * position base_index + i) or by RN (ASR_ROUND_RN).
+ *
+ * tensors      host array of n_tensors descriptors (read during the call only);
+ *              buffers of different tensors must not overlap.
+ * lr           >= 0, finite.       beta1, beta2   in [0, 1).
+ * eps          >= 0, finite.       weight_decay   >= 0, finite.
+ * step         1-based step count t, in [1, 2**32 - 1]; used for the bias
+ *              corrections and as key word 1.
+ * seed         key word 0.
+ * workspace    device buffer of at least asr_adamw_workspace_bytes(n_tensors)
+ *              bytes, 16-byte aligned, owned by the caller. Its contents are
+ *              overwritten (stream-ordered); it must not be used by other
+ *              work that runs concurrently with this step.
+ * Errors: ASR_EINVAL (n_tensors < 0, NULL tensors with n_tensors > 0,
+ * numel < 0, a NULL buffer in a non-empty tensor, hyperparameter or step out
+ * of range, rounding code unknown, more than 2**47 elements of one dtype
+ * pair), ASR_EDTYPE, ASR_EALIGN (param/grad not aligned to 2 or 4 bytes as
+ * their dtype needs, m/v not 4-byte aligned), ASR_EWORKSPACE, ASR_EHIP.
+ * Tensors whose four buffers are 16-byte aligned take the 128-bit path;
+ * others are processed element by element with identical results.
+ */
+int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors,
+                   double lr, double beta1, double beta2, double eps,
+                   double weight_decay, int64_t step, uint32_t seed,
+                   int32_t rounding, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * The eight binary32 constants asr_adamw_step uses for these
+ * hyperparameters, in this order: decay, b1, omb1, b2, omb2, step_size,
+ * inv_bc2_sqrt, eps32 (see asr_adamw_step). Host only; touches no device.
+ * out: host array of 8 floats. Errors: ASR_EINVAL as for asr_adamw_step.
+ */
+int asr_adamw_host_scalars(double lr, double beta1, double beta2, double eps,
+                           double weight_decay, int64_t step, float* out);
+
+/*
+ * Philox4x32-10 words of n_counters consecutive counters.
+ * ("Add stochastic rounding and philox RNG helpers", Primitives.)
+ * Call k (0 <= k < n_counters) uses counter
+ *   (lo32(c), hi32(c), lo32(counter_upper), hi32(counter_upper)),
+ *   c = counter_base + k (mod 2**64),
+ * and key (seed, step); its words 0..3 go to out[4k .. 4k+3].
+ * With counter_upper = 0 these are the calls of the random-bit stream.
+ * out: device buffer of 4*n_counters uint32, 4-byte aligned.
+ * Errors: ASR_EINVAL (n_counters < 0, out NULL with n_counters > 0),
+ * ASR_EALIGN, ASR_EHIP.
+ */
+int asr_philox_4x32_fill(uint32_t* out, int64_t n_counters,
+                         uint64_t counter_base, uint64_t counter_upper,
+                         uint32_t seed, uint32_t step, void* stream);
+
+/*
+ * Stochastic-rounding conversion f32 -> bf16 of n elements.
+ * ("Add stochastic rounding and philox RNG helpers", Primitives and
+ * discussion: SR as a rounding mode of the conversion.)
+ * out[i] = SR(in[i], r16(base_index + i)) with key (seed, step).
+ * in: device, n f32, 4-byte aligned; out: device, n bf16 patterns, 2-byte
+ * aligned; in and out must not overlap.
+ * Errors: ASR_EINVAL (n < 0, NULL buffer with n > 0), ASR_EALIGN, ASR_EHIP.
+ */
+int asr_cvt_f32_bf16_sr(const float* in, uint16_t* out, int64_t n,
+                        uint32_t seed, uint32_t step, uint64_t base_index,
+                        void* stream);
+
+/*
+ * Round-to-nearest-even conversion f32 -> bf16 (the comparison mode; the
+ * FlyDSL page's Consumer section keeps "rn" as the default rounding).
+ * Same buffers and errors as asr_cvt_f32_bf16_sr.
+ */
+int asr_cvt_f32_bf16_rn(const float* in, uint16_t* out, int64_t n,
+                        void* stream);
+
+/*
+ * Test support: the binary32 square root and division exactly as the AdamW
+ * kernel evaluates them: sqrt_out[i] = sqrt(a[i]), div_out[i] = a[i] / b[i],
+ * both correctly rounded (to nearest even, subnormals kept).
+ * All buffers: device, n floats, 4-byte aligned.
+ * Errors: ASR_EINVAL, ASR_EALIGN, ASR_EHIP.
+ */
+int asr_f32_sqrt_div(const float* a, const float* b, float* sqrt_out,
+                     float* div_out, int64_t n, void* stream);
+
+/* Text for the last non-OK status returned on this thread ("" if none). The
+ * pointer stays valid until the next library call on this thread. */
+const char* asr_last_error(void);
+
+/* ABI version of this header and library (major * 100 + minor). */
+int asr_abi_version(void);
+
+#define ASR_ABI_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAMW_SR_H */

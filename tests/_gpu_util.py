@@ -1,0 +1,72 @@
+"""Helpers shared by the GPU tests: moving seeded inputs between host and
+device and comparing bit patterns. No arithmetic of the method lives here."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from adamw_optimizer_stochastic_amd import workloads as wl
+
+gpu = pytest.mark.gpu
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def announce(*parts):
+    """Name the case before the GPU runs it (flushed, so a fault still shows it)."""
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def f32_tensor(x, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def bf16_tensor(bits, device="cuda"):
+    return wl.bf16_bits_to_tensor(bits, device)
+
+
+def to_host(t):
+    """Device tensor -> numpy: bf16 -> uint16 patterns, f32 -> float32,
+    int32 -> uint32."""
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.int32:
+        return t.cpu().numpy().view(np.uint32)
+    return t.cpu().numpy()
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a.view(np.uint32)
+    return a
+
+
+def assert_bits_equal(got, want, what=""):
+    g, w = bits(got), bits(want)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    bad = np.nonzero(g != w)[0]
+    if bad.size:
+        i = bad[:8]
+        raise AssertionError(f"{what}: {bad.size} of {g.size} differ; first at {i.tolist()}: "
+                             f"got {[hex(int(x)) for x in g[i]]} want {[hex(int(x)) for x in w[i]]}")
+
+
+def assert_f32_equal_or_both_nan(got, want, what=""):
+    g = np.ascontiguousarray(got, dtype=np.float32)
+    w = np.ascontiguousarray(want, dtype=np.float32)
+    both_nan = np.isnan(g) & np.isnan(w)
+    assert_bits_equal(np.where(both_nan, np.float32(0), g), np.where(both_nan, np.float32(0), w),
+                      what)
+
+
+def bf16_is_nan(h):
+    h = np.asarray(h, dtype=np.uint16)
+    return ((h & 0x7F80) == 0x7F80) & ((h & 0x7F) != 0)

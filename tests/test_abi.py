@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (CPU only; no call here launches a kernel).
+
+  * the library loads and exports every entry point include/adamw_sr.h
+    declares, and the ctypes struct matches the C layout;
+  * the binary32 constants the library forms on the host equal the
+    oracle's bit for bit over a grid of hyperparameters and steps;
+  * argument errors come back as the documented status codes, before any
+    device work (these calls return early, so no GPU is needed).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from adamw_optimizer_stochastic_amd import _abi, _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adamw_sr.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not _build.is_built():
+        _build.build()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(asr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert "asr_adamw_step" in names and "asr_philox_4x32_fill" in names
+    assert "asr_cvt_f32_bf16_sr" in names
+    lib = ctypes.CDLL(_build.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) <= set(_abi._SIGNATURES), "binding lacks a declared entry point"
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(_abi.AsrTensor) == 56
+    assert _abi.AsrTensor.base_index.offset == 40
+    assert _abi.AsrTensor.param_dtype.offset == 48
+    assert _abi.asr_abi_version() == _abi.ABI_VERSION
+
+
+def test_workspace_bytes():
+    assert _abi.asr_adamw_workspace_bytes(0) == 0
+    assert _abi.asr_adamw_workspace_bytes(-3) == 0
+    prev = 0
+    for n in [1, 2, 7, 64, 291, 5000]:
+        b = _abi.asr_adamw_workspace_bytes(n)
+        assert b >= 56 * n + 4 * (n + 1) and b % 256 == 0 and b >= prev
+        prev = b
+
+
+@pytest.mark.parametrize("lr,b1,b2,eps,wd", [
+    (1e-3, 0.9, 0.999, 1e-8, 0.01), (1e-4, 0.9, 0.999, 1e-8, 0.0),
+    (3e-3, 0.9, 0.95, 1e-6, 0.1), (0.0, 0.0, 0.0, 0.0, 0.0), (7.5e-2, 0.5, 0.99999, 1e-3, 5.0)])
+def test_host_scalars_match_oracle(lr, b1, b2, eps, wd):
+    for t in [1, 2, 3, 10, 100, 1000, 6000, 65537, 2**31 - 1, 2**32 - 1]:
+        lib_vals = np.array(_abi.asr_adamw_host_scalars(lr, b1, b2, eps, wd, t), np.float32)
+        sc = oracle.host_scalars(lr, b1, b2, eps, wd, t)
+        want = np.array([sc.decay, sc.b1, sc.omb1, sc.b2, sc.omb2, sc.step_size,
+                         sc.inv_bc2_sqrt, sc.eps], np.float32)
+        assert np.array_equal(lib_vals.view(np.uint32), want.view(np.uint32)), t
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except _abi.AsrError as e:
+        return e.status
+    return _abi.ASR_OK
+
+
+def _t(**kw):
+    d = dict(param=0x1000, grad=0x2000, exp_avg=0x3000, exp_avg_sq=0x4000, numel=8,
+             base_index=0, param_dtype=_abi.ASR_BF16, grad_dtype=_abi.ASR_BF16)
+    d.update(kw)
+    return d
+
+
+HP = (1e-3, 0.9, 0.999, 1e-8, 0.01)
+
+
+def _step(tensors, hp=HP, step=1, rounding=0, ws=0x10000, ws_bytes=1 << 20):
+    return _status(_abi.asr_adamw_step, tensors, *hp, step, 0, rounding, ws, ws_bytes, None)
+
+
+def test_step_argument_errors():
+    E = _abi
+    assert _step([_t(numel=-1)]) == E.ASR_EINVAL
+    assert _step([_t(param=0)]) == E.ASR_EINVAL
+    assert _step([_t(param_dtype=2)]) == E.ASR_EDTYPE
+    assert _step([_t(grad_dtype=-1)]) == E.ASR_EDTYPE
+    assert _step([_t(param=0x1001)]) == E.ASR_EALIGN          # bf16 needs 2 bytes
+    assert _step([_t(param_dtype=0, param=0x1002)]) == E.ASR_EALIGN   # f32 needs 4
+    assert _step([_t(exp_avg=0x3002)]) == E.ASR_EALIGN
+    assert _step([_t()], step=0) == E.ASR_EINVAL
+    assert _step([_t()], step=2**32) == E.ASR_EINVAL
+    assert _step([_t()], rounding=2) == E.ASR_EINVAL
+    assert _step([_t()], hp=(-1e-3, 0.9, 0.999, 1e-8, 0.01)) == E.ASR_EINVAL
+    assert _step([_t()], hp=(1e-3, 1.0, 0.999, 1e-8, 0.01)) == E.ASR_EINVAL
+    assert _step([_t()], hp=(1e-3, 0.9, -0.1, 1e-8, 0.01)) == E.ASR_EINVAL
+    assert _step([_t()], hp=(1e-3, 0.9, 0.999, float("nan"), 0.01)) == E.ASR_EINVAL
+    assert _step([_t()], hp=(1e-3, 0.9, 0.999, 1e-8, float("inf"))) == E.ASR_EINVAL
+    assert _step([_t()], ws=0) == E.ASR_EWORKSPACE
+    assert _step([_t()], ws_bytes=16) == E.ASR_EWORKSPACE
+    assert _step([_t()], ws=0x10008) == E.ASR_EWORKSPACE
+    assert "workspace" in _abi.asr_last_error()
+    # Nothing to do: an empty list, or only empty tensors, is a no-op.
+    assert _step([]) == E.ASR_OK
+    assert _step([_t(numel=0, param=0, grad=0)], ws=0, ws_bytes=0) == E.ASR_OK
+    assert _abi.asr_last_error() == ""
+
+
+def test_other_entry_points_argument_errors():
+    E = _abi
+    assert _status(_abi.asr_philox_4x32_fill, 0x1000, -1, 0, 0, 0, 0, None) == E.ASR_EINVAL
+    assert _status(_abi.asr_philox_4x32_fill, 0, 4, 0, 0, 0, 0, None) == E.ASR_EINVAL
+    assert _status(_abi.asr_philox_4x32_fill, 0x1002, 4, 0, 0, 0, 0, None) == E.ASR_EALIGN
+    assert _status(_abi.asr_philox_4x32_fill, 0, 0, 0, 0, 0, 0, None) == E.ASR_OK
+    assert _status(_abi.asr_cvt_f32_bf16_sr, 0x1000, 0x2000, -5, 0, 0, 0, None) == E.ASR_EINVAL
+    assert _status(_abi.asr_cvt_f32_bf16_sr, 0x1002, 0x2000, 5, 0, 0, 0, None) == E.ASR_EALIGN
+    assert _status(_abi.asr_cvt_f32_bf16_sr, 0x1000, 0x2001, 5, 0, 0, 0, None) == E.ASR_EALIGN
+    assert _status(_abi.asr_cvt_f32_bf16_rn, 0, 0x2000, 5, None) == E.ASR_EINVAL
+    assert _status(_abi.asr_cvt_f32_bf16_rn, 0, 0, 0, None) == E.ASR_OK
+    assert _status(_abi.asr_f32_sqrt_div, 0x1000, 0x2000, 0x3000, 0x4001, 3, None) == E.ASR_EALIGN
+    assert _status(_abi.asr_f32_sqrt_div, 0, 0, 0, 0, -1, None) == E.ASR_EINVAL
+    assert _status(_abi.asr_adamw_host_scalars, 1e-3, 0.9, 0.999, 1e-8, 0.01, 0) == E.ASR_EINVAL

@@ -1,0 +1,308 @@
+"""GPU parity of the fused AdamW step through the C ABI, against the oracle.
+
+Bar: bit-exact on f32 m/v/params and bf16 params (the kernel follows the
+oracle's binary32 operation order, without fused multiply-adds, with
+correctly rounded sqrt and division). Where an input makes a NaN, the NaN's
+payload is not specified by IEEE 754 for arithmetic results, so only
+NaN-ness is compared there.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.adamw import F32, BF16, ROUND_SR, ROUND_RN
+from adamw_optimizer_stochastic_amd import ops, AdamWSR
+from adamw_optimizer_stochastic_amd import workloads as wl
+from _gpu_util import (gpu, require_gpu, announce, f32_tensor, bf16_tensor, to_host,
+                       assert_bits_equal, assert_f32_equal_or_both_nan, bf16_is_nan)
+
+pytestmark = gpu
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _host_tensor(rng, n, dtype, std):
+    x = wl.normal_f32(rng, n, std)
+    return wl.f32_to_bf16_bits(x) if dtype == BF16 else x
+
+
+def _to_dev(x, dtype):
+    return bf16_tensor(x) if dtype == BF16 else f32_tensor(x)
+
+
+def _check_outputs(dev, want, pdt, what, nan_ok=False):
+    p_t, m_t, v_t = dev
+    p_w, m_w, v_w = want
+    cmp = assert_f32_equal_or_both_nan if nan_ok else assert_bits_equal
+    cmp(to_host(m_t), m_w, what + " m")
+    cmp(to_host(v_t), v_w, what + " v")
+    if pdt == BF16:
+        got = to_host(p_t)
+        if nan_ok:
+            nan = bf16_is_nan(got) & bf16_is_nan(p_w)
+            got, p_w = np.where(nan, 0, got), np.where(nan, 0, p_w)
+        assert_bits_equal(got, p_w, what + " param")
+    else:
+        cmp(to_host(p_t), p_w, what + " param")
+
+
+def test_small_bf16_10_steps():
+    """65,536 bf16 params, fresh bf16 grads each step, 10 SR steps."""
+    n = 65536
+    rng = wl.host_rng(wl.CFG_SMALL, 0, 0)
+    p = _host_tensor(rng, n, BF16, 0.02)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    pd, md, vd = bf16_tensor(p), f32_tensor(m), f32_tensor(v)
+    for t in range(1, 11):
+        announce("small bf16 step", t)
+        g = _host_tensor(wl.host_rng(wl.CFG_SMALL, 0, t), n, BF16, 1e-3)
+        p, m, v = oracle.step_tensor(p, g, m, v, param_dtype=BF16, grad_dtype=BF16, base_index=0,
+                                     step=t, seed=0, **HP)
+        ops.adamw_step([pd], [bf16_tensor(g)], [md], [vd], [0], step=t, seed=0,
+                       beta1=HP["beta1"], beta2=HP["beta2"], lr=HP["lr"], eps=HP["eps"],
+                       weight_decay=HP["weight_decay"])
+        _check_outputs((pd, md, vd), (p, m, v), BF16, f"step {t}")
+
+
+@pytest.mark.parametrize("pdt,gdt", [(F32, F32), (BF16, BF16), (BF16, F32), (F32, BF16)])
+@pytest.mark.parametrize("rounding", [ROUND_SR, ROUND_RN])
+def test_dtype_pairs_ragged_list(pdt, gdt, rounding):
+    """A list of ragged sizes (several chunks, ragged tails) with odd and
+    large base indices, a few steps, one dtype pair per list."""
+    sizes = [1, 7, 8, 9, 2047, 2049, 4096 + 3, 70001, 300007]
+    bases = [0, 5, (1 << 32) - 3, 1 << 33, (1 << 34) + 1, 3, 17, 2, (1 << 40) + 7]
+    rng = wl.host_rng(wl.CFG_SMALL, 100 + pdt * 4 + gdt * 2 + rounding, 0)
+    host = []
+    dev = []
+    for n, b in zip(sizes, bases):
+        p = _host_tensor(rng, n, pdt, 0.02)
+        m = wl.normal_f32(rng, n, 1e-4)
+        v = np.abs(wl.normal_f32(rng, n, 1e-7))
+        host.append([p, m, v, b])
+        dev.append([_to_dev(p, pdt), f32_tensor(m), f32_tensor(v)])
+    for t in (1, 2, 7):
+        announce("ragged list", pdt, gdt, rounding, "step", t)
+        grads_h = [_host_tensor(rng, n, gdt, 1e-3) for n in sizes]
+        grads_d = [_to_dev(g, gdt) for g in grads_h]
+        rmode = "sr" if rounding == ROUND_SR else "rn"
+        ops.adamw_step([d[0] for d in dev], grads_d, [d[1] for d in dev], [d[2] for d in dev],
+                       bases, step=t, seed=9, rounding=rmode, **HP)
+        for k, (h, g) in enumerate(zip(host, grads_h)):
+            h[0], h[1], h[2] = oracle.step_tensor(h[0], g, h[1], h[2], param_dtype=pdt,
+                                                  grad_dtype=gdt, base_index=h[3], step=t, seed=9,
+                                                  rounding=rounding, **HP)
+            _check_outputs(dev[k], h[:3], pdt, f"tensor {k} (n={sizes[k]}) step {t}")
+
+
+def test_mixed_dtype_list_one_call():
+    """All four dtype pairs in one call (one launch per pair)."""
+    announce("mixed dtype list")
+    rng = wl.host_rng(wl.CFG_SMALL, 7, 0)
+    specs = [(BF16, BF16, 10000), (F32, F32, 3001), (BF16, F32, 5), (F32, BF16, 65537),
+             (BF16, BF16, 0), (BF16, BF16, 129)]
+    host, dev, base = [], [], 0
+    for pdt, gdt, n in specs:
+        p = _host_tensor(rng, n, pdt, 0.02)
+        g = _host_tensor(rng, n, gdt, 1e-3)
+        m = wl.normal_f32(rng, n, 1e-4)
+        v = np.abs(wl.normal_f32(rng, n, 1e-7))
+        host.append((p, g, m, v, base, pdt, gdt))
+        dev.append((_to_dev(p, pdt), _to_dev(g, gdt), f32_tensor(m), f32_tensor(v)))
+        base += n
+    ops.adamw_step([d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev],
+                   [d[3] for d in dev], [h[4] for h in host], step=3, seed=1, **HP)
+    for k, (p, g, m, v, b, pdt, gdt) in enumerate(host):
+        want = oracle.step_tensor(p, g, m, v, param_dtype=pdt, grad_dtype=gdt, base_index=b,
+                                  step=3, seed=1, **HP)
+        _check_outputs(dev[k][:1] + dev[k][2:], want, pdt, f"tensor {k}")
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3, 5])
+def test_unaligned_views_take_elementwise_path(offset):
+    """Views starting `offset` elements into their storage are not 16-byte
+    aligned; results must not change."""
+    announce("unaligned views", offset)
+    n = 10000
+    rng = wl.host_rng(wl.CFG_SMALL, 50 + offset, 0)
+    p = _host_tensor(rng, n + offset, BF16, 0.02)
+    g = _host_tensor(rng, n + offset, BF16, 1e-3)
+    m = wl.normal_f32(rng, n + offset, 1e-4)
+    v = np.abs(wl.normal_f32(rng, n + offset, 1e-7))
+    pd, gd, md, vd = bf16_tensor(p), bf16_tensor(g), f32_tensor(m), f32_tensor(v)
+    base = 1001
+    ops.adamw_step([pd[offset:]], [gd[offset:]], [md[offset:]], [vd[offset:]], [base], step=5,
+                   seed=4, **HP)
+    want = oracle.step_tensor(p[offset:], g[offset:], m[offset:], v[offset:], param_dtype=BF16,
+                              grad_dtype=BF16, base_index=base, step=5, seed=4, **HP)
+    _check_outputs((pd[offset:], md[offset:], vd[offset:]), want, BF16, "unaligned")
+    assert_bits_equal(to_host(pd[:offset]), p[:offset], "untouched head")
+
+
+def test_extreme_values_nan_inf_subnormal():
+    """Grads and states across the exponent range, with Inf/NaN injected."""
+    announce("extreme values")
+    rng = np.random.default_rng(5)
+    n = 50000
+    def edge(k):
+        x = (rng.choice([-1.0, 1.0], k) * rng.uniform(1, 2, k) *
+             np.exp2(rng.integers(-149, 100, k).astype(np.float64))).astype(np.float32)
+        return x
+    p = edge(n)
+    g = edge(n)
+    m = edge(n)
+    v = np.abs(edge(n))
+    g.view(np.uint32)[::97] = 0x7F800000
+    g.view(np.uint32)[::101] = 0x7FC00000
+    p.view(np.uint32)[::103] = 0xFF800000
+    for pdt in (F32, BF16):
+        pp = wl.f32_to_bf16_bits(p) if pdt == BF16 else p
+        pd, gd, md, vd = _to_dev(pp, pdt), f32_tensor(g), f32_tensor(m), f32_tensor(v)
+        ops.adamw_step([pd], [gd], [md], [vd], [77], step=12, seed=3, lr=1e-2, beta1=0.9,
+                       beta2=0.95, eps=1e-6, weight_decay=0.1)
+        want = oracle.step_tensor(pp, g, m, v, param_dtype=pdt, grad_dtype=F32, base_index=77,
+                                  step=12, seed=3, lr=1e-2, beta1=0.9, beta2=0.95, eps=1e-6,
+                                  weight_decay=0.1)
+        _check_outputs((pd, md, vd), want, pdt, f"extreme pdt={pdt}", nan_ok=True)
+
+
+def test_f32_100_steps_vs_oracle_and_torch():
+    """f32 params and grads (the f32 workload at 2**20 elements): 100 steps,
+    bit-exact against the oracle and within the page's 1e-4 of
+    torch.optim.AdamW (adamw-sr page, Correctness section)."""
+    n, T = 1 << 20, 100
+    rng = wl.host_rng(wl.CFG_F32, 0, 0)
+    p = wl.normal_f32(rng, n, 0.02)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    pd, md, vd = f32_tensor(p), f32_tensor(m), f32_tensor(v)
+    tp = torch.nn.Parameter(f32_tensor(p))
+    topt = torch.optim.AdamW([tp], **{"lr": 1e-3, "betas": (0.9, 0.999), "eps": 1e-8,
+                                      "weight_decay": 0.01})
+    for t in range(1, T + 1):
+        g = wl.normal_f32(wl.host_rng(wl.CFG_F32, 0, t), n, 1e-2)
+        gd = f32_tensor(g)
+        ops.adamw_step([pd], [gd], [md], [vd], [0], step=t, seed=0, **HP)
+        tp.grad = gd.clone()
+        topt.step()
+        if t in (1, 50, 100):
+            announce("f32 step", t)
+    p_o = wl.normal_f32(wl.host_rng(wl.CFG_F32, 0, 0), n, 0.02)
+    m_o = np.zeros(n, np.float32)
+    v_o = np.zeros(n, np.float32)
+    for t in range(1, T + 1):
+        g = wl.normal_f32(wl.host_rng(wl.CFG_F32, 0, t), n, 1e-2)
+        p_o, m_o, v_o = oracle.step_tensor(p_o, g, m_o, v_o, param_dtype=F32, grad_dtype=F32,
+                                           base_index=0, step=t, seed=0, **HP)
+    _check_outputs((pd, md, vd), (p_o, m_o, v_o), F32, "after 100 steps")
+    diff = (pd - tp.detach()).abs().max().item()
+    assert diff < 1e-4, diff
+
+
+def test_subulp_accumulation_full_size():
+    """The sub-ULP example at 1,048,576 bf16 params and 6,000 steps (adamw-sr
+    page, intro): RN never leaves 1.0, SR climbs toward 1.5, repeats are
+    bitwise identical; a 1,024-element window is checked against the oracle
+    bit for bit over all 6,000 steps."""
+    n, T, lr = 1 << 20, 6000, 1e-4
+    win0, win = 123456, 1024
+
+    def run(rounding, seed):
+        w = torch.full((n,), 1.0, dtype=torch.bfloat16, device="cuda")
+        m = torch.zeros(n, dtype=torch.float32, device="cuda")
+        v = torch.zeros(n, dtype=torch.float32, device="cuda")
+        ws = ops.make_workspace(1, "cuda")
+        for t in range(1, T + 1):
+            g = w.float() - 1.5                       # exact in binary32
+            ops.adamw_step([w], [g], [m], [v], [0], lr=lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                           weight_decay=0.0, step=t, seed=seed, rounding=rounding, workspace=ws)
+        return to_host(w)
+
+    announce("subulp rn")
+    rn = run("rn", 0)
+    assert np.all(rn == 0x3F80)
+    announce("subulp sr")
+    sr = run("sr", 0)
+    announce("subulp sr repeat")
+    assert np.array_equal(sr, run("sr", 0))
+    mean = oracle.bf16_to_f32(sr).astype(np.float64).mean()
+    assert 1.40 < mean < 1.5, mean
+
+    hw = np.full(win, 0x3F80, np.uint16)
+    hm = np.zeros(win, np.float32)
+    hv = np.zeros(win, np.float32)
+    for t in range(1, T + 1):
+        g = oracle.bf16_to_f32(hw) - np.float32(1.5)
+        hw, hm, hv = oracle.step_tensor(hw, g, hm, hv, param_dtype=BF16, grad_dtype=F32,
+                                        base_index=win0, lr=lr, beta1=0.9, beta2=0.999,
+                                        eps=1e-8, weight_decay=0.0, step=t, seed=0)
+    assert_bits_equal(sr[win0:win0 + win], hw, "window after 6000 steps")
+
+
+def test_optimizer_class_matches_oracle_and_resumes():
+    """AdamWSR over a small bf16 model: base_index = running numel in
+    parameter order, params without grads are skipped, and a state_dict
+    round trip resumes bit for bit."""
+    announce("AdamWSR class")
+    torch.manual_seed(0)
+    model = torch.nn.Sequential(torch.nn.Linear(64, 96), torch.nn.ReLU(),
+                                torch.nn.Linear(96, 10)).cuda().to(torch.bfloat16)
+    params = list(model.parameters())
+    opt = AdamWSR(model.parameters(), lr=1e-3, weight_decay=0.01, seed=5)
+    host = [[wl.tensor_to_bf16_bits(p.detach().reshape(-1)),
+             np.zeros(p.numel(), np.float32), np.zeros(p.numel(), np.float32)] for p in params]
+    bases = np.cumsum([0] + [p.numel() for p in params])[:-1]
+    for k, b in enumerate(bases):
+        assert opt.base_index(params[k]) == b
+    steps = [0] * len(params)
+    for it in range(3):
+        x = torch.randn(32, 64, device="cuda", dtype=torch.bfloat16)
+        opt.zero_grad()
+        model(x).float().square().mean().backward()
+        if it == 1:
+            params[1].grad = None                     # skipped this step
+        grads = [None if p.grad is None else wl.tensor_to_bf16_bits(p.grad.reshape(-1))
+                 for p in params]
+        opt.step()
+        for k, g in enumerate(grads):
+            if g is None:
+                continue
+            steps[k] += 1
+            h = host[k]
+            h[0], h[1], h[2] = oracle.step_tensor(h[0], g, h[1], h[2], param_dtype=BF16,
+                                                  grad_dtype=BF16, base_index=int(bases[k]),
+                                                  step=steps[k], seed=5, **HP)
+    for k, p in enumerate(params):
+        assert_bits_equal(wl.tensor_to_bf16_bits(p.detach().reshape(-1)), host[k][0], f"param {k}")
+        assert_bits_equal(to_host(opt.state[p]["exp_avg"]), host[k][1], f"m {k}")
+    # Resume: a fresh optimizer loaded from the state dict continues identically.
+    sd = opt.state_dict()
+    clone = torch.nn.Sequential(torch.nn.Linear(64, 96), torch.nn.ReLU(),
+                                torch.nn.Linear(96, 10)).cuda().to(torch.bfloat16)
+    clone.load_state_dict(model.state_dict())
+    opt2 = AdamWSR(clone.parameters(), lr=1e-3, weight_decay=0.01, seed=0)
+    opt2.load_state_dict(sd)
+    assert opt2.seed == 5
+    x = torch.randn(32, 64, device="cuda", dtype=torch.bfloat16)
+    for mdl, o in ((model, opt), (clone, opt2)):
+        o.zero_grad()
+        mdl(x).float().square().mean().backward()
+        o.step()
+    for a, b in zip(model.parameters(), clone.parameters()):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_optimizer_rejects_unsupported_options():
+    with pytest.raises(NotImplementedError):
+        AdamWSR([torch.zeros(4, device="cuda", requires_grad=True)], amsgrad=True)
+    with pytest.raises(NotImplementedError):
+        AdamWSR([torch.zeros(4, device="cuda", dtype=torch.float16, requires_grad=True)])
+    with pytest.raises(ValueError):
+        AdamWSR([torch.zeros(4, device="cuda", requires_grad=True)], seed=1 << 32)

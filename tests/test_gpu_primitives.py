@@ -1,0 +1,153 @@
+"""GPU parity of the primitives through the C ABI: Philox words, the SR and
+RN conversions, and the binary32 sqrt/division the AdamW kernel uses.
+Bit-exact against the oracle (integer work and correctly rounded f32)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adamw_optimizer_stochastic_amd import ops
+from adamw_optimizer_stochastic_amd import workloads as wl
+from _gpu_util import (gpu, require_gpu, announce, f32_tensor, to_host, assert_bits_equal,
+                       assert_f32_equal_or_both_nan)
+
+pytestmark = gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------- Philox
+@pytest.mark.parametrize("n,base,upper,seed,step", [
+    (1 << 24, 0, 0, 0, 1),
+    (1000, 0, 0, 0xFFFFFFFF, 0xFFFFFFFF),
+    ((1 << 16) + 13, (1 << 32) - 3, 0, 7, 0),
+    ((1 << 16) + 1, (1 << 34) + 5, 0, 123456789, 6000),
+    (4099, (1 << 64) - 7, 0, 1, 2),                   # counter wraps modulo 2**64
+    (2053, 12345, (5 << 32) | 3, 99, 3),              # counter words 2 and 3 in use
+    (1, 0, 0, 0, 0),
+])
+def test_philox_fill_bit_exact(n, base, upper, seed, step):
+    announce("philox_fill", n, base, upper, seed, step)
+    got = to_host(ops.philox_4x32_fill(n, base, seed, step, counter_upper=upper))
+    want = oracle.philox_fill(n, base, seed, step, counter_upper=upper)
+    assert_bits_equal(got, want, "philox words")
+
+
+def test_philox_fill_unaligned_output():
+    announce("philox_fill unaligned out")
+    buf = torch.zeros(4 * 513 + 1, dtype=torch.int32, device="cuda")
+    out = buf[1:]                                   # 4-byte but not 16-byte aligned
+    ops.philox_4x32_fill(513, 77, 5, 6, out=out)
+    got = to_host(buf)
+    assert got[0] == 0
+    assert_bits_equal(got[1:], oracle.philox_fill(513, 77, 5, 6), "philox words (unaligned)")
+
+
+# ------------------------------------------------------------ conversions
+SIZES = [1, 3, 8, 9, 2047, 2048, 2053, (1 << 20) + 13]
+BASES = [0, 1, 3, 5, (1 << 32) - 3, (1 << 32) + 5, (1 << 34) - 3, (1 << 34) + 5]
+
+
+def _convert_input(n, seed):
+    rng = wl.host_rng(wl.CFG_CONVERT, seed, n)
+    x = rng.standard_normal(n).astype(np.float32)
+    if n >= 20:
+        wl.inject_specials(x, 0.05, rng)
+        # subnormals, exact bf16 values and ties
+        x.view(np.uint32)[:8] = [0x00000001, 0x80008000, 0x3F808000, 0x3F818000, 0x7F7F0000,
+                                 0x00000000, 0x80000000, 0x007FFFFF]
+    return x
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("base", BASES)
+def test_cvt_sr_bit_exact(n, base):
+    announce("cvt_sr", n, base)
+    x = _convert_input(n, 1)
+    got = to_host(ops.cvt_f32_bf16_sr(f32_tensor(x), 7, 0, base))
+    assert_bits_equal(got, oracle.cvt_f32_bf16_sr(x, 7, 0, base), "cvt sr")
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_cvt_rn_bit_exact(n):
+    announce("cvt_rn", n)
+    x = _convert_input(n, 2)
+    got = to_host(ops.cvt_f32_bf16_rn(f32_tensor(x)))
+    assert_bits_equal(got, oracle.cvt_f32_bf16_rn(x), "cvt rn")
+
+
+@pytest.mark.parametrize("offset_in,offset_out", [(1, 0), (0, 1), (3, 5)])
+def test_cvt_unaligned_views(offset_in, offset_out):
+    announce("cvt unaligned", offset_in, offset_out)
+    n = 5000
+    x = _convert_input(n + offset_in, 3)
+    xin = f32_tensor(x)[offset_in:]
+    out_buf = torch.zeros(n + offset_out, dtype=torch.bfloat16, device="cuda")
+    ops.cvt_f32_bf16_sr(xin, 11, 4, 33, out=out_buf[offset_out:])
+    got = to_host(out_buf)
+    assert np.all(got[:offset_out] == 0)
+    assert_bits_equal(got[offset_out:], oracle.cvt_f32_bf16_sr(x[offset_in:], 11, 4, 33), "cvt")
+
+
+def test_cvt_sr_seed_and_step_change_bits():
+    announce("cvt seed/step sensitivity")
+    x = f32_tensor(np.random.default_rng(0).standard_normal(1 << 16).astype(np.float32))
+    a = to_host(ops.cvt_f32_bf16_sr(x, 1, 1))
+    b = to_host(ops.cvt_f32_bf16_sr(x, 2, 1))
+    c = to_host(ops.cvt_f32_bf16_sr(x, 1, 2))
+    a2 = to_host(ops.cvt_f32_bf16_sr(x, 1, 1))
+    assert np.array_equal(a, a2)
+    # Each element rounds up with probability = its dropped fraction, so two
+    # keys disagree on a good share of the elements.
+    assert (a != b).mean() > 0.2 and (a != c).mean() > 0.2
+
+
+def test_cvt_sr_statistics_on_device():
+    """The device's SR of one value repeated over many positions: outputs on
+    the two neighbours only, up-fraction matching the dropped bits within
+    binomial bounds (the FlyDSL page's device tests)."""
+    announce("cvt sr statistics")
+    n = 1 << 22
+    for pattern in (0x3F80_4000, 0x3F80_0001, 0xBF7F_C000, 0x0000_9000):
+        x = torch.full((n,), 0.0, dtype=torch.float32, device="cuda")
+        x.view(torch.int32).fill_(np.uint32(pattern).view(np.int32).item())
+        out = to_host(ops.cvt_f32_bf16_sr(x, 3, 5))
+        hi = pattern >> 16
+        assert set(np.unique(out).tolist()) <= {hi, hi + 1}
+        p = (pattern & 0xFFFF) / 65536.0
+        ups = (out == hi + 1).mean()
+        assert abs(ups - p) < 6 * np.sqrt(p * (1 - p) / n) + 1e-9, (hex(pattern), ups, p)
+
+
+# ------------------------------------------------------ sqrt / division
+def test_sqrt_div_random_patterns_bit_exact():
+    announce("sqrt/div random patterns")
+    rng = np.random.default_rng(42)
+    n = 1 << 24
+    a = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    b = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    # Also plain positive values of every binade, as the AdamW kernel sees them.
+    a[: n // 4] = np.abs(a[: n // 4])
+    s, d = ops.f32_sqrt_div(f32_tensor(a), f32_tensor(b))
+    with np.errstate(all="ignore"):
+        want_s = np.sqrt(a)
+        want_d = np.divide(a, b)
+    assert_f32_equal_or_both_nan(to_host(s), want_s, "sqrt")
+    assert_f32_equal_or_both_nan(to_host(d), want_d, "div")
+
+
+def test_sqrt_exhaustive_nonnegative():
+    """Every non-negative f32 pattern (2**31 inputs, in slices)."""
+    announce("sqrt exhaustive")
+    step = 1 << 27
+    ones = torch.ones(step, dtype=torch.float32, device="cuda")
+    for start in range(0, 1 << 31, step):
+        u = torch.arange(start, start + step, dtype=torch.int64, device="cuda").to(torch.int32)
+        a = u.view(torch.float32)
+        s, _ = ops.f32_sqrt_div(a, ones)
+        host = np.arange(start, start + step, dtype=np.uint32).view(np.float32)
+        assert_f32_equal_or_both_nan(to_host(s), np.sqrt(host), f"sqrt slice {start:#x}")
