@@ -47,7 +47,7 @@ _c = ctypes
 _SIGNATURES = {
     "asr_abi_version": (_c.c_int, []),
     "asr_last_error": (_c.c_char_p, []),
-    "asr_adamw_workspace_bytes": (_c.c_size_t, [_c.c_int32]),
+    "asr_adamw_workspace_bytes": (_c.c_size_t, [_c.POINTER(AsrTensor), _c.c_int32]),
     "asr_adamw_host_scalars": (_c.c_int, [_c.c_double] * 5 + [_c.c_int64, _c.POINTER(_c.c_float)]),
     "asr_adamw_step": (_c.c_int, [_c.POINTER(AsrTensor), _c.c_int32] + [_c.c_double] * 5 +
                        [_c.c_int64, _c.c_uint32, _c.c_int32, _c.c_void_p, _c.c_size_t,
@@ -98,8 +98,18 @@ def asr_last_error():
     return lib().asr_last_error().decode(errors="replace")
 
 
-def asr_adamw_workspace_bytes(n_tensors):
-    return int(lib().asr_adamw_workspace_bytes(n_tensors))
+def _tensor_array(tensors):
+    n = len(tensors)
+    arr = (AsrTensor * max(n, 1))()
+    for i, t in enumerate(tensors):
+        arr[i] = t if isinstance(t, AsrTensor) else AsrTensor(**t)
+    return arr, n
+
+
+def asr_adamw_workspace_bytes(tensors):
+    """tensors: sequence of AsrTensor (or dicts); only numel is read."""
+    arr, n = _tensor_array(tensors)
+    return int(lib().asr_adamw_workspace_bytes(arr if n else None, n))
 
 
 def asr_adamw_host_scalars(lr, beta1, beta2, eps, weight_decay, step):
@@ -114,10 +124,7 @@ def asr_adamw_host_scalars(lr, beta1, beta2, eps, weight_decay, step):
 def asr_adamw_step(tensors, lr, beta1, beta2, eps, weight_decay, step, seed, rounding,
                    workspace, workspace_bytes, stream):
     """tensors: sequence of AsrTensor (or of dicts with its field names)."""
-    n = len(tensors)
-    arr = (AsrTensor * max(n, 1))()
-    for i, t in enumerate(tensors):
-        arr[i] = t if isinstance(t, AsrTensor) else AsrTensor(**t)
+    arr, n = _tensor_array(tensors)
     _check(lib().asr_adamw_step(arr if n else None, n, lr, beta1, beta2, eps, weight_decay,
                                 step, seed, rounding, workspace, workspace_bytes, stream),
            "asr_adamw_step")

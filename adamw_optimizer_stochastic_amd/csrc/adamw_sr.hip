@@ -24,6 +24,7 @@
 #include <adamw_sr.h>
 
 #include <algorithm>
+#include <map>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -36,20 +37,31 @@
 
 namespace asr {
 
-constexpr int kBlock = 256;           // 4 waves of 64 lanes
-constexpr int kVec = 8;               // elements per lane per iteration
-constexpr int kMinChunkShift = 11;    // one block-iteration: 256 * 8 elements
-#ifndef ASR_MAX_CHUNK_SHIFT
-#define ASR_MAX_CHUNK_SHIFT 16
+constexpr int kBlock = 256;            // 4 waves of 64 lanes
+#ifndef ASR_VEC
+#define ASR_VEC 4
 #endif
-constexpr int kMaxChunkShift = ASR_MAX_CHUNK_SHIFT;
-#ifndef ASR_TARGET_CHUNKS
-#define ASR_TARGET_CHUNKS 32768
+constexpr int kVec = ASR_VEC;          // elements per lane of the step kernel
+constexpr int kCvtVec = 8;             // elements per lane of the converts
+constexpr int64_t kSlot = kBlock * kVec;  // elements per workgroup of the step kernel
+// Blocks per launch; a larger list is covered by several launches.
+constexpr uint32_t kMaxGrid = 1u << 23;
+// Resident workgroups per CU for the step kernel. The path is bound by HBM
+// with seven concurrent streams (four read, three written); measured on
+// MI355X, the DRAM works best when the whole chip moves through one narrow
+// window of addresses with about 24 KiB of loads in flight per CU, and four
+// resident 4-element-per-lane workgroups keep that while hiding each slot's
+// arithmetic (about 6.1 TB/s on a single large tensor, against 5.2 TB/s with
+// the CU filled). The cap is applied by reserving LDS at launch (160 KiB per
+// CU on gfx950); the kernel itself uses none.
+#ifndef ASR_BLOCKS_PER_CU
+#define ASR_BLOCKS_PER_CU 4
 #endif
-constexpr int64_t kTargetChunks = ASR_TARGET_CHUNKS;
-constexpr uint32_t kMaxGrid = 1u << 20;  // blocks; larger work grid-strides
-constexpr int kGroups = 4;               // (param dtype, grad dtype) pairs
-constexpr int kUploadWords = 768;        // 3 KiB of metadata per upload launch
+constexpr int kBlocksPerCU = ASR_BLOCKS_PER_CU;
+constexpr uint32_t kLdsPerCU = 160u * 1024u;
+constexpr bool kNonTemporal = false;   // streaming hints measured slower here
+constexpr int kGroups = 4;             // (param dtype, grad dtype) pairs
+constexpr int kUploadWords = 768;      // 3 KiB of metadata per upload launch
 
 // Per-tensor metadata as the kernel reads it from the workspace.
 struct DevTensor {
@@ -59,137 +71,142 @@ struct DevTensor {
   float* v;
   int64_t numel;
   uint64_t base_index;
-  uint32_t vec_ok;  // all four buffers 16-byte aligned: 128-bit path
-  uint32_t reserved;
+  uint32_t vec_ok;      // all four buffers 16-byte aligned: 128-bit path
+  uint32_t first_slot;  // index of the tensor's first slot within its group
 };
 static_assert(sizeof(DevTensor) == 56, "metadata layout");
 
-// ------------------------------------------------------- uniform loads
-// Metadata is the same for the whole workgroup; keep it in scalar registers.
-__device__ __forceinline__ uint32_t uniform_u32(const uint32_t* p) {
-  return __builtin_amdgcn_readfirstlane(*p);
-}
-__device__ __forceinline__ uint64_t uniform_u64(const uint64_t* p) {
-  const uint64_t x = *p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-__device__ __forceinline__ DevTensor uniform_tensor(const DevTensor* t) {
-  const uint64_t* w = reinterpret_cast<const uint64_t*>(t);
-  DevTensor d;
-  d.param = reinterpret_cast<void*>(uniform_u64(w + 0));
-  d.grad = reinterpret_cast<const void*>(uniform_u64(w + 1));
-  d.m = reinterpret_cast<float*>(uniform_u64(w + 2));
-  d.v = reinterpret_cast<float*>(uniform_u64(w + 3));
-  d.numel = static_cast<int64_t>(uniform_u64(w + 4));
-  d.base_index = uniform_u64(w + 5);
-  const uint64_t flags = uniform_u64(w + 6);
-  d.vec_ok = static_cast<uint32_t>(flags);
-  d.reserved = 0;
-  return d;
-}
-
 enum : int { kRoundSR = ASR_ROUND_SR, kRoundRN = ASR_ROUND_RN };
 
-// One span [start, stop) of one tensor; each lane takes 8 consecutive
-// elements per iteration, the block strides by 2048 elements.
+// One lane's kVec consecutive elements i0 .. i0+kVec-1 of tensor t (count of
+// them inside the tensor: 0..kVec). VEC: the tensor's buffers are 16-byte
+// aligned, so a full run moves with vector accesses (128-bit for f32; 128- or
+// 64-bit for bf16); otherwise element by element.
 template <class PT, class GT, int ROUND, int PHASE, bool VEC>
-__device__ __forceinline__ void adamw_span(const DevTensor& t, int64_t start,
-                                           int64_t stop, const Coeffs& c,
-                                           uint32_t seed, uint32_t step) {
+__device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int count,
+                                           const Coeffs& c, uint32_t seed, uint32_t step) {
   using PS = typename PT::storage;
   using GS = typename GT::storage;
-  PS* __restrict__ param = static_cast<PS*>(t.param);
-  const GS* __restrict__ grad = static_cast<const GS*>(t.grad);
-  float* __restrict__ m = t.m;
-  float* __restrict__ v = t.v;
-  for (int64_t i0 = start + static_cast<int64_t>(threadIdx.x) * kVec; i0 < stop;
-       i0 += static_cast<int64_t>(kBlock) * kVec) {
-    const int64_t left = stop - i0;
-    const int count = left < kVec ? static_cast<int>(left) : kVec;
-    const bool full = VEC && count == kVec;
-    float p[kVec], g[kVec], mm[kVec], vv[kVec];
-    if (full) {
-      load8(param + i0, p);
-      load8(grad + i0, g);
-      load8(m + i0, mm);
-      load8(v + i0, vv);
-    } else {
-      load_n(param + i0, count, p);
-      load_n(grad + i0, count, g);
-      load_n(m + i0, count, mm);
-      load_n(v + i0, count, vv);
-    }
+  PS* __restrict__ param = static_cast<PS*>(t.param) + i0;
+  const GS* __restrict__ grad = static_cast<const GS*>(t.grad) + i0;
+  float* __restrict__ m = t.m + i0;
+  float* __restrict__ v = t.v + i0;
+  const bool full = VEC && count == kVec;
+  float p[kVec], g[kVec], mm[kVec], vv[kVec];
+  if (full) {
+    load_vec<kNonTemporal, kVec>(param, p);
+    load_vec<kNonTemporal, kVec>(grad, g);
+    load_vec<kNonTemporal, kVec>(m, mm);
+    load_vec<kNonTemporal, kVec>(v, vv);
+  } else {
+    load_n(param, count, p);
+    load_n(grad, count, g);
+    load_n(m, count, mm);
+    load_n(v, count, vv);
+  }
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) adamw_update(p[e], g[e], mm[e], vv[e], c);
+  for (int e = 0; e < kVec; ++e) adamw_update(p[e], g[e], mm[e], vv[e], c);
 
-    if constexpr (std::is_same_v<PT, F32>) {
-      if (full) store8(param + i0, p);
-      else store_n(param + i0, count, p);
-    } else {
-      uint32_t h[kVec];
-      if constexpr (ROUND == kRoundSR) {
-        uint32_t r[kVec];
-        stream_bits8<PHASE>(t.base_index + static_cast<uint64_t>(i0), seed, step, r);
+  if constexpr (std::is_same_v<PT, F32>) {
+    if (full) store_vec<kNonTemporal, kVec>(param, p);
+    else store_n(param, count, p);
+  } else {
+    uint32_t h[kVec];
+    if constexpr (ROUND == kRoundSR) {
+      uint32_t r[kVec];
+      stream_bits<PHASE, kVec>(t.base_index + static_cast<uint64_t>(i0), seed, step, r);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) h[e] = round_sr(__float_as_uint(p[e]), r[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) h[e] = round_rn(__float_as_uint(p[e]));
-      }
-      if (full) store8_bf16(param + i0, h);
-      else store_n_bf16(param + i0, count, h);
-    }
-    if (full) {
-      store8(m + i0, mm);
-      store8(v + i0, vv);
+      for (int e = 0; e < kVec; ++e) h[e] = round_sr(__float_as_uint(p[e]), r[e]);
     } else {
-      store_n(m + i0, count, mm);
-      store_n(v + i0, count, vv);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) h[e] = round_rn(__float_as_uint(p[e]));
     }
+    if (full) store_vec_bf16<kNonTemporal, kVec>(param, h);
+    else store_n_bf16(param, count, h);
+  }
+  if (full) {
+    store_vec<kNonTemporal, kVec>(m, mm);
+    store_vec<kNonTemporal, kVec>(v, vv);
+  } else {
+    store_n(m, count, mm);
+    store_n(v, count, vv);
   }
 }
 
 template <class PT, class GT, int ROUND, bool VEC>
-__device__ __forceinline__ void adamw_span_phase(const DevTensor& t, int64_t start,
-                                                 int64_t stop, const Coeffs& c,
-                                                 uint32_t seed, uint32_t step) {
+__device__ __forceinline__ void adamw_run_phase(const DevTensor& t, int64_t i0, int count,
+                                                 const Coeffs& c, uint32_t seed, uint32_t step) {
   if constexpr (std::is_same_v<PT, BF16> && ROUND == kRoundSR) {
     switch (static_cast<int>(t.base_index & 3u)) {
-      case 0: adamw_span<PT, GT, ROUND, 0, VEC>(t, start, stop, c, seed, step); break;
-      case 1: adamw_span<PT, GT, ROUND, 1, VEC>(t, start, stop, c, seed, step); break;
-      case 2: adamw_span<PT, GT, ROUND, 2, VEC>(t, start, stop, c, seed, step); break;
-      default: adamw_span<PT, GT, ROUND, 3, VEC>(t, start, stop, c, seed, step); break;
+      case 0: adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, count, c, seed, step); break;
+      case 1: adamw_run<PT, GT, ROUND, 1, VEC>(t, i0, count, c, seed, step); break;
+      case 2: adamw_run<PT, GT, ROUND, 2, VEC>(t, i0, count, c, seed, step); break;
+      default: adamw_run<PT, GT, ROUND, 3, VEC>(t, i0, count, c, seed, step); break;
     }
   } else {
-    adamw_span<PT, GT, ROUND, 0, VEC>(t, start, stop, c, seed, step);
+    adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, count, c, seed, step);
   }
 }
 
-// The multi-tensor step. chunk_begin[k] is the first chunk of tensor k
-// (chunk_begin[0] = 0, chunk_begin[n_tensors] = n_chunks, every tensor has at
-// least one chunk); a chunk is 2**chunk_shift consecutive elements of one
-// tensor, the last one of a tensor possibly shorter.
+// Slot `local` (kSlot elements) of tensor t: one kVec-element run per lane.
+// Lanes past the end of a short last slot get count 0 and touch nothing (no
+// early exit, so the whole descriptor is fetched in one round).
+template <class PT, class GT, int ROUND>
+__device__ __forceinline__ void adamw_slot(const DevTensor& t, uint32_t local, const Coeffs& c,
+                                           uint32_t seed, uint32_t step) {
+  const int64_t i0 = static_cast<int64_t>(local) * kSlot + static_cast<int64_t>(threadIdx.x) * kVec;
+  const int64_t left = t.numel - i0;
+  const int count = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
+  if (t.vec_ok) adamw_run_phase<PT, GT, ROUND, true>(t, i0, count, c, seed, step);
+  else adamw_run_phase<PT, GT, ROUND, false>(t, i0, count, c, seed, step);
+}
+
+// The multi-tensor step, one slot per workgroup, no loop: the workgroups in
+// flight (dispatched in order) sweep the memory as one narrow window. All
+// descriptor reads come before any store and have uniform addresses, so they
+// are scalar loads.
+//
+// Size-class form: every tensor of the launch has the same numel, so slot s
+// belongs to tensor s / slots_per_tensor. The quotient is taken as the high
+// half of s * magic, magic = floor((2**32 - 1) / slots_per_tensor), which
+// falls short of the true quotient by at most one (s < 2**32), then
+// corrected; the descriptor table is small and stays in the scalar cache.
 template <class PT, class GT, int ROUND>
 __global__ void __launch_bounds__(kBlock)
-adamw_sr_multi_tensor(const DevTensor* __restrict__ tensors,
-                      const uint32_t* __restrict__ chunk_begin, int32_t n_tensors,
-                      uint32_t n_chunks, int32_t chunk_shift, Coeffs c,
-                      uint32_t seed, uint32_t step) {
-  for (uint32_t chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {
-    int32_t lo = 0, hi = n_tensors - 1;  // last tensor whose first chunk <= chunk
+adamw_sr_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_tensor, uint32_t magic,
+               uint32_t slot0, Coeffs c, uint32_t seed, uint32_t step) {
+  const uint32_t slot = slot0 + blockIdx.x;
+  uint32_t ti = __umulhi(slot, magic);
+  if (static_cast<uint64_t>(ti + 1) * slots_per_tensor <= slot) ++ti;
+  const DevTensor t = tensors[ti];
+  adamw_slot<PT, GT, ROUND>(t, slot - ti * slots_per_tensor, c, seed, step);
+}
+
+// Table form, for tensors of any sizes: slot_tensor[s] names the tensor of
+// slot s (filled on the device from the tensors' first slots).
+template <class PT, class GT, int ROUND>
+__global__ void __launch_bounds__(kBlock)
+adamw_sr_slots(const DevTensor* __restrict__ tensors, const uint32_t* __restrict__ slot_tensor,
+               uint32_t slot0, Coeffs c, uint32_t seed, uint32_t step) {
+  const uint32_t slot = slot0 + blockIdx.x;
+  const DevTensor t = tensors[slot_tensor[slot]];
+  adamw_slot<PT, GT, ROUND>(t, slot - t.first_slot, c, seed, step);
+}
+
+// slot_tensor[s] = the last k with first_slot[k] <= s (first_slot ascending,
+// first_slot[0] = 0, every tensor at least one slot).
+__global__ void __launch_bounds__(kBlock)
+fill_slot_table(const uint32_t* __restrict__ first_slot, int32_t n_tensors,
+                uint32_t* __restrict__ slot_tensor, uint32_t n_slots) {
+  const uint32_t stride = gridDim.x * kBlock;
+  for (uint32_t s = blockIdx.x * kBlock + threadIdx.x; s < n_slots; s += stride) {
+    int32_t lo = 0, hi = n_tensors - 1;
     while (lo < hi) {
       const int32_t mid = (lo + hi + 1) >> 1;
-      if (uniform_u32(chunk_begin + mid) <= chunk) lo = mid;
+      if (first_slot[mid] <= s) lo = mid;
       else hi = mid - 1;
     }
-    const DevTensor t = uniform_tensor(tensors + lo);
-    const int64_t start =
-        static_cast<int64_t>(chunk - uniform_u32(chunk_begin + lo)) << chunk_shift;
-    const int64_t stop = std::min(start + (int64_t{1} << chunk_shift), t.numel);
-    if (t.vec_ok) adamw_span_phase<PT, GT, ROUND, true>(t, start, stop, c, seed, step);
-    else adamw_span_phase<PT, GT, ROUND, false>(t, start, stop, c, seed, step);
+    slot_tensor[s] = static_cast<uint32_t>(lo);
   }
 }
 
@@ -231,26 +248,27 @@ __device__ __forceinline__ void convert_all(const float* __restrict__ in,
                                             uint16_t* __restrict__ out, int64_t n,
                                             uint64_t base_index, uint32_t seed,
                                             uint32_t step) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock * kVec;
-  for (int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * kVec; i0 < n;
+  constexpr int V = kCvtVec;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock * V;
+  for (int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * V; i0 < n;
        i0 += stride) {
     const int64_t left = n - i0;
-    const int count = left < kVec ? static_cast<int>(left) : kVec;
-    const bool full = VEC && count == kVec;
-    float x[kVec];
-    if (full) load8(in + i0, x);
+    const int count = left < V ? static_cast<int>(left) : V;
+    const bool full = VEC && count == V;
+    float x[V];
+    if (full) load_vec<kNonTemporal, V>(in + i0, x);
     else load_n(in + i0, count, x);
-    uint32_t h[kVec];
+    uint32_t h[V];
     if constexpr (ROUND == kRoundSR) {
-      uint32_t r[kVec];
-      stream_bits8<PHASE>(base_index + static_cast<uint64_t>(i0), seed, step, r);
+      uint32_t r[V];
+      stream_bits<PHASE, V>(base_index + static_cast<uint64_t>(i0), seed, step, r);
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) h[e] = round_sr(__float_as_uint(x[e]), r[e]);
+      for (int e = 0; e < V; ++e) h[e] = round_sr(__float_as_uint(x[e]), r[e]);
     } else {
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) h[e] = round_rn(__float_as_uint(x[e]));
+      for (int e = 0; e < V; ++e) h[e] = round_rn(__float_as_uint(x[e]));
     }
-    if (full) store8_bf16(out + i0, h);
+    if (full) store_vec_bf16<kNonTemporal, V>(out + i0, h);
     else store_n_bf16(out + i0, count, h);
   }
 }
@@ -314,17 +332,23 @@ int ok() {
 // Launches `kernel` with one block size for all kernels of the library;
 // the arguments are converted to the kernel's parameter types first.
 template <typename... KArgs, typename... Args>
-hipError_t launch(void (*kernel)(KArgs...), uint32_t grid, hipStream_t stream,
-                  Args&&... args) {
+hipError_t launch_lds(void (*kernel)(KArgs...), uint32_t grid, uint32_t lds_bytes,
+                      hipStream_t stream, Args&&... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
   std::tuple<KArgs...> vals(std::forward<Args>(args)...);
   return std::apply(
       [&](auto&... v) {
         void* argv[] = {static_cast<void*>(&v)...};
         return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid),
-                               dim3(asr::kBlock), argv, 0, stream);
+                               dim3(asr::kBlock), argv, lds_bytes, stream);
       },
       vals);
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), uint32_t grid, hipStream_t stream,
+                  Args&&... args) {
+  return launch_lds(kernel, grid, 0, stream, std::forward<Args>(args)...);
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -379,49 +403,157 @@ asr::Coeffs make_coeffs(double lr, double beta1, double beta2, double eps, doubl
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: for each (param dtype, grad dtype) group in a fixed
-// order, its DevTensor array then its chunk_begin array, each 16-byte
-// aligned. The bound below covers any split of n tensors into the groups.
-size_t workspace_bound(int32_t n) {
+uint64_t slots_of(int64_t numel) {
+  return (static_cast<uint64_t>(numel) + asr::kSlot - 1) / asr::kSlot;
+}
+
+// A (param dtype, grad dtype) pair's tensors are launched as size classes
+// (equal numel, at least kClassMinSlots slots in total; up to
+// kMaxClassLaunches per pair) plus one table-driven launch for the rest.
+constexpr uint64_t kClassMinSlots = 2048;
+constexpr int kMaxClassLaunches = 64;
+constexpr int kMaxLaunches = asr::kGroups * (kMaxClassLaunches + 1);
+
+// Workspace layout: first every launch's DevTensor array and (table
+// launches) its first_slot array, each 16-byte aligned (this prefix is
+// uploaded from the host); then every table launch's slot table, filled on
+// the device. The bound covers any split of the tensors into launches.
+size_t workspace_bound(int32_t n, uint64_t total_slots) {
   if (n <= 0) return 0;
-  const size_t per_group_pad = 2 * 16;
+  const size_t pad = 3 * 16 * static_cast<size_t>(kMaxLaunches);
   return align_up(static_cast<size_t>(n) * sizeof(asr::DevTensor) +
-                      (static_cast<size_t>(n) + asr::kGroups) * sizeof(uint32_t) +
-                      asr::kGroups * per_group_pad,
+                      static_cast<size_t>(n) * sizeof(uint32_t) +
+                      static_cast<size_t>(total_slots) * sizeof(uint32_t) + pad,
                   256);
 }
 
-int chunk_shift_for(int64_t total) {
-  int s = asr::kMinChunkShift;
-  while (s < asr::kMaxChunkShift && ((total + (int64_t{1} << s) - 1) >> s) > asr::kTargetChunks)
-    ++s;
-  return s;
+struct Launch {
+  int group = 0;
+  bool by_class = false;
+  std::vector<asr::DevTensor> tensors;
+  uint32_t slots_per_tensor = 0;  // size-class launches
+  uint64_t n_slots = 0;
+  size_t tensors_off = 0, first_off = 0, table_off = 0;
+};
+
+// Splits each dtype pair into size-class launches and one table launch.
+// Returns an empty string or an error message.
+std::string plan_launches(const std::vector<asr::DevTensor> (&group)[asr::kGroups],
+                          std::vector<Launch>* out) {
+  for (int g = 0; g < asr::kGroups; ++g) {
+    if (group[g].empty()) continue;
+    std::map<int64_t, std::vector<size_t>> by_numel;
+    for (size_t i = 0; i < group[g].size(); ++i) by_numel[group[g][i].numel].push_back(i);
+    Launch rest;
+    rest.group = g;
+    int classes = 0;
+    for (const auto& [numel, idx] : by_numel) {
+      const uint64_t per = slots_of(numel);
+      const uint64_t total = per * idx.size();
+      if (total >= kClassMinSlots && classes < kMaxClassLaunches) {
+        if (total > 0xFFFFFFFFull) return "more than 2**32 slots of one size";
+        Launch l;
+        l.group = g;
+        l.by_class = true;
+        l.slots_per_tensor = static_cast<uint32_t>(per);
+        l.n_slots = total;
+        for (size_t i : idx) {
+          asr::DevTensor d = group[g][i];
+          d.first_slot = static_cast<uint32_t>(l.tensors.size() * per);
+          l.tensors.push_back(d);
+        }
+        out->push_back(std::move(l));
+        ++classes;
+      } else {
+        for (size_t i : idx) {
+          asr::DevTensor d = group[g][i];
+          d.first_slot = static_cast<uint32_t>(rest.n_slots);
+          rest.tensors.push_back(d);
+          rest.n_slots += per;
+          if (rest.n_slots > 0xFFFFFFFFull) return "more than 2**32 slots of mixed sizes";
+        }
+      }
+    }
+    if (!rest.tensors.empty()) out->push_back(std::move(rest));
+  }
+  return "";
 }
 
-hipError_t launch_group(int group, int rounding, const asr::DevTensor* d_tensors,
-                        const uint32_t* d_begin, int32_t n, uint32_t n_chunks,
-                        int32_t shift, const asr::Coeffs& c, uint32_t seed,
-                        uint32_t step, hipStream_t stream) {
-  const uint32_t grid = std::min(n_chunks, asr::kMaxGrid);
+using TableKernel = void (*)(const asr::DevTensor*, const uint32_t*, uint32_t, asr::Coeffs,
+                             uint32_t, uint32_t);
+using ClassKernel = void (*)(const asr::DevTensor*, uint32_t, uint32_t, uint32_t, asr::Coeffs,
+                             uint32_t, uint32_t);
+
+template <template <class, class, int> class Pick>
+auto pick_kernel(int group, int rounding) {
   using asr::BF16;
   using asr::F32;
-  using K = void (*)(const asr::DevTensor*, const uint32_t*, int32_t, uint32_t, int32_t,
-                     asr::Coeffs, uint32_t, uint32_t);
-  K k = nullptr;
   const bool sr = rounding == ASR_ROUND_SR;
   switch (group) {
-    case ASR_F32 * 2 + ASR_F32: k = asr::adamw_sr_multi_tensor<F32, F32, asr::kRoundSR>; break;
-    case ASR_F32 * 2 + ASR_BF16: k = asr::adamw_sr_multi_tensor<F32, BF16, asr::kRoundSR>; break;
+    case ASR_F32 * 2 + ASR_F32: return Pick<F32, F32, asr::kRoundSR>::get();
+    case ASR_F32 * 2 + ASR_BF16: return Pick<F32, BF16, asr::kRoundSR>::get();
     case ASR_BF16 * 2 + ASR_F32:
-      k = sr ? asr::adamw_sr_multi_tensor<BF16, F32, asr::kRoundSR>
-             : asr::adamw_sr_multi_tensor<BF16, F32, asr::kRoundRN>;
-      break;
+      return sr ? Pick<BF16, F32, asr::kRoundSR>::get() : Pick<BF16, F32, asr::kRoundRN>::get();
     default:
-      k = sr ? asr::adamw_sr_multi_tensor<BF16, BF16, asr::kRoundSR>
-             : asr::adamw_sr_multi_tensor<BF16, BF16, asr::kRoundRN>;
-      break;
+      return sr ? Pick<BF16, BF16, asr::kRoundSR>::get() : Pick<BF16, BF16, asr::kRoundRN>::get();
   }
-  return launch(k, grid, stream, d_tensors, d_begin, n, n_chunks, shift, c, seed, step);
+}
+template <class PT, class GT, int R>
+struct PickTable {
+  static TableKernel get() { return asr::adamw_sr_slots<PT, GT, R>; }
+};
+template <class PT, class GT, int R>
+struct PickClass {
+  static ClassKernel get() { return asr::adamw_sr_class<PT, GT, R>; }
+};
+
+// LDS reserved per workgroup to hold the step kernel at kBlocksPerCU
+// resident workgroups per CU (0 = no cap).
+hipError_t occupancy_lds(const void* kernel, uint32_t* lds) {
+  *lds = 0;
+  if (asr::kBlocksPerCU <= 0) return hipSuccess;
+  *lds = (asr::kLdsPerCU / asr::kBlocksPerCU) & ~1023u;
+  if (*lds > 64u * 1024u)
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(*lds));
+  return hipSuccess;
+}
+
+// One launch of the plan: (table launches) the slot table, then the step in
+// launches of at most kMaxGrid slots.
+hipError_t run_launch(const Launch& l, uint8_t* ws, int rounding, const asr::Coeffs& c,
+                      uint32_t seed, uint32_t step, hipStream_t stream) {
+  const auto* d_tensors = reinterpret_cast<const asr::DevTensor*>(ws + l.tensors_off);
+  const uint32_t n_slots = static_cast<uint32_t>(l.n_slots);
+  hipError_t e;
+  uint32_t lds = 0;
+  if (l.by_class) {
+    const ClassKernel k = pick_kernel<PickClass>(l.group, rounding);
+    if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
+    const uint32_t magic = 0xFFFFFFFFu / l.slots_per_tensor;
+    for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
+      const uint32_t grid = std::min(n_slots - slot0, asr::kMaxGrid);
+      e = launch_lds(k, grid, lds, stream, d_tensors, l.slots_per_tensor, magic, slot0, c, seed,
+                     step);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  auto* d_table = reinterpret_cast<uint32_t*>(ws + l.table_off);
+  const uint32_t fill_grid = std::min<uint32_t>((n_slots + asr::kBlock - 1) / asr::kBlock, 4096u);
+  e = launch(asr::fill_slot_table, fill_grid, stream,
+             reinterpret_cast<const uint32_t*>(ws + l.first_off),
+             static_cast<int32_t>(l.tensors.size()), d_table, n_slots);
+  if (e != hipSuccess) return e;
+  const TableKernel k = pick_kernel<PickTable>(l.group, rounding);
+  if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
+  for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
+    const uint32_t grid = std::min(n_slots - slot0, asr::kMaxGrid);
+    e = launch_lds(k, grid, lds, stream, d_tensors, static_cast<const uint32_t*>(d_table), slot0,
+                   c, seed, step);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -432,7 +564,13 @@ int asr_abi_version(void) { return ASR_ABI_VERSION; }
 
 const char* asr_last_error(void) { return g_last_error.c_str(); }
 
-size_t asr_adamw_workspace_bytes(int32_t n_tensors) { return workspace_bound(n_tensors); }
+size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors) {
+  if (n_tensors <= 0 || !tensors) return 0;
+  uint64_t slots = 0;
+  for (int32_t i = 0; i < n_tensors; ++i)
+    if (tensors[i].numel > 0) slots += slots_of(tensors[i].numel);
+  return workspace_bound(n_tensors, slots);
+}
 
 int asr_adamw_host_scalars(double lr, double beta1, double beta2, double eps,
                            double weight_decay, int64_t step, float* out) {
@@ -456,7 +594,7 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, doub
 
   // Validate and sort into dtype groups; drop empty tensors.
   std::vector<asr::DevTensor> group[asr::kGroups];
-  int64_t group_elems[asr::kGroups] = {0, 0, 0, 0};
+  uint64_t group_slots[asr::kGroups] = {0, 0, 0, 0};
   for (int32_t i = 0; i < n_tensors; ++i) {
     const asr_tensor& t = tensors[i];
     const std::string at = "tensor " + std::to_string(i) + ": ";
@@ -482,54 +620,62 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, doub
     d.base_index = t.base_index;
     d.vec_ok = aligned(t.param, 16) && aligned(t.grad, 16) && aligned(t.exp_avg, 16) &&
                aligned(t.exp_avg_sq, 16);
-    d.reserved = 0;
+    d.first_slot = 0;  // set by the launch plan
     group[g].push_back(d);
-    group_elems[g] += t.numel;
-    if (group_elems[g] > (int64_t{1} << 47))
-      return fail(ASR_EINVAL, "more than 2**47 elements of one dtype pair");
+    group_slots[g] += slots_of(t.numel);
+    if (group_slots[g] > 0xFFFFFFFFull)
+      return fail(ASR_EINVAL, "more than 2**32 slots of one dtype pair");
   }
-  int64_t total = 0;
-  for (int g = 0; g < asr::kGroups; ++g) total += group_elems[g];
-  if (total == 0) return ok();
+  uint64_t total_slots = 0;
+  for (int g = 0; g < asr::kGroups; ++g) total_slots += group_slots[g];
+  if (total_slots == 0) return ok();
 
-  const size_t need = workspace_bound(n_tensors);
+  const size_t need = workspace_bound(n_tensors, total_slots);
   if (!workspace || workspace_bytes < need)
     return fail(ASR_EWORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
   if (!aligned(workspace, 16)) return fail(ASR_EWORKSPACE, "workspace not 16-byte aligned");
 
-  const int shift = chunk_shift_for(total);
+  std::vector<Launch> launches;
+  const std::string err = plan_launches(group, &launches);
+  if (!err.empty()) return fail(ASR_EINVAL, err);
   const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
 
-  // Build the host image of the table.
-  std::vector<uint8_t> image(need, 0);
+  // Workspace offsets: uploaded metadata first, device-filled tables after.
   size_t off = 0;
-  size_t tensors_off[asr::kGroups], begin_off[asr::kGroups];
-  uint32_t n_chunks[asr::kGroups] = {0, 0, 0, 0};
-  for (int g = 0; g < asr::kGroups; ++g) {
-    if (group[g].empty()) continue;
+  for (Launch& l : launches) {
     off = align_up(off, 16);
-    tensors_off[g] = off;
-    std::memcpy(image.data() + off, group[g].data(), group[g].size() * sizeof(asr::DevTensor));
-    off += group[g].size() * sizeof(asr::DevTensor);
-    off = align_up(off, 16);
-    begin_off[g] = off;
-    uint64_t chunks = 0;
-    for (size_t k = 0; k <= group[g].size(); ++k) {
-      const uint32_t b = static_cast<uint32_t>(chunks);
-      std::memcpy(image.data() + off + k * sizeof(uint32_t), &b, sizeof(b));
-      if (k < group[g].size())
-        chunks += (static_cast<uint64_t>(group[g][k].numel) + (uint64_t{1} << shift) - 1) >> shift;
+    l.tensors_off = off;
+    off += l.tensors.size() * sizeof(asr::DevTensor);
+    if (!l.by_class) {
+      off = align_up(off, 16);
+      l.first_off = off;
+      off += l.tensors.size() * sizeof(uint32_t);
     }
-    n_chunks[g] = static_cast<uint32_t>(chunks);
-    off += (group[g].size() + 1) * sizeof(uint32_t);
+  }
+  const size_t meta_bytes = align_up(off, 16);
+  off = meta_bytes;
+  for (Launch& l : launches) {
+    if (l.by_class) continue;
+    off = align_up(off, 16);
+    l.table_off = off;
+    off += l.n_slots * sizeof(uint32_t);
+  }
+  if (off > need) return fail(ASR_EWORKSPACE, "internal: workspace plan exceeds its bound");
+  std::vector<uint8_t> image(meta_bytes, 0);
+  for (const Launch& l : launches) {
+    std::memcpy(image.data() + l.tensors_off, l.tensors.data(),
+                l.tensors.size() * sizeof(asr::DevTensor));
+    if (!l.by_class)
+      for (size_t k = 0; k < l.tensors.size(); ++k)
+        std::memcpy(image.data() + l.first_off + k * sizeof(uint32_t), &l.tensors[k].first_slot,
+                    sizeof(uint32_t));
   }
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const size_t used = align_up(off, sizeof(uint32_t));
-  for (size_t pos = 0; pos < used; pos += asr::kUploadWords * sizeof(uint32_t)) {
+  for (size_t pos = 0; pos < meta_bytes; pos += asr::kUploadWords * sizeof(uint32_t)) {
     asr::UploadBlock blk;
-    const size_t bytes = std::min(used - pos, sizeof(blk.w));
+    const size_t bytes = std::min(meta_bytes - pos, sizeof(blk.w));
     std::memset(blk.w, 0, sizeof(blk.w));
     std::memcpy(blk.w, image.data() + pos, bytes);
     hipError_t e = launch(asr::upload_words, 1, stream, blk,
@@ -537,13 +683,8 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, doub
                           static_cast<uint32_t>(bytes / sizeof(uint32_t)));
     if (e != hipSuccess) return hip_fail(e, "metadata upload launch");
   }
-  for (int g = 0; g < asr::kGroups; ++g) {
-    if (group[g].empty()) continue;
-    hipError_t e = launch_group(
-        g, rounding, reinterpret_cast<const asr::DevTensor*>(ws + tensors_off[g]),
-        reinterpret_cast<const uint32_t*>(ws + begin_off[g]),
-        static_cast<int32_t>(group[g].size()), n_chunks[g], shift, c, seed,
-        static_cast<uint32_t>(step), stream);
+  for (const Launch& l : launches) {
+    hipError_t e = run_launch(l, ws, rounding, c, seed, static_cast<uint32_t>(step), stream);
     if (e != hipSuccess) return hip_fail(e, "adamw kernel launch");
   }
   return ok();
@@ -575,7 +716,7 @@ static int convert(int rounding, const float* in, uint16_t* out, int64_t n, uint
   if (!aligned(in, 4) || !aligned(out, 2))
     return fail(ASR_EALIGN, "buffer not aligned to its element size");
   if (n > (int64_t{1} << 62)) return fail(ASR_EINVAL, "n too large");
-  const int64_t blocks = (n + asr::kBlock * asr::kVec - 1) / (asr::kBlock * asr::kVec);
+  const int64_t blocks = (n + asr::kBlock * asr::kCvtVec - 1) / (asr::kBlock * asr::kCvtVec);
   const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(blocks, 1 << 16));
   const int vec_ok = aligned(in, 16) && aligned(out, 16);
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);

@@ -64,32 +64,24 @@ __device__ __forceinline__ Words4 stream_call(uint64_t j, uint32_t seed,
                        0u, 0u, seed, step);
 }
 
-// 16 random bits for the 8 consecutive positions pos0 .. pos0+7, where
+// 16 random bits for the V consecutive positions pos0 .. pos0+V-1, where
 // PHASE = pos0 & 3 is known at compile time. Position pos0+e takes word
-// (PHASE+e) & 3 of call (pos0 >> 2) + ((PHASE+e) >> 2): two calls when the
-// run starts on a group of four, three otherwise.
-template <int PHASE>
-__device__ __forceinline__ void stream_bits8(uint64_t pos0, uint32_t seed,
-                                             uint32_t step, uint32_t (&r)[8]) {
+// (PHASE+e) & 3 of call (pos0 >> 2) + ((PHASE+e) >> 2): V/4 calls when the
+// run starts on a group of four, one more otherwise.
+template <int PHASE, int V>
+__device__ __forceinline__ void stream_bits(uint64_t pos0, uint32_t seed, uint32_t step,
+                                            uint32_t (&r)[V]) {
+  constexpr int kCalls = (PHASE + V + 3) / 4;
   const uint64_t j0 = pos0 >> 2;
-  const Words4 a = stream_call(j0, seed, step);
-  const Words4 b = stream_call(j0 + 1, seed, step);
-  uint32_t words[12];
+  uint32_t words[4 * kCalls];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    words[k] = a.w[k];
-    words[4 + k] = b.w[k];
-  }
-  if constexpr (PHASE != 0) {
-    const Words4 c = stream_call(j0 + 2, seed, step);
+  for (int k = 0; k < kCalls; ++k) {
+    const Words4 w = stream_call(j0 + k, seed, step);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) words[8 + k] = c.w[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) words[8 + k] = 0u;
+    for (int q = 0; q < 4; ++q) words[4 * k + q] = w.w[q];
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = words[PHASE + e] & 0xFFFFu;
+  for (int e = 0; e < V; ++e) r[e] = words[PHASE + e] & 0xFFFFu;
 }
 
 // ------------------------------------------------------------- roundings
@@ -145,57 +137,99 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
 }
 
 // 128-bit loads/stores of 8 elements starting at a 16-byte-aligned address.
-__device__ __forceinline__ void load8(const float* src, float (&x)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(src)[0];
-  const float4 b = reinterpret_cast<const float4*>(src)[1];
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+// NT selects the non-temporal (streaming) form: every byte of the step is
+// touched exactly once, so there is nothing to gain from keeping it cached.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT, typename V>
+__device__ __forceinline__ V vload(const V* src) {
+  if constexpr (NT) return __builtin_nontemporal_load(src);
+  else return *src;
 }
 
-__device__ __forceinline__ void load8(const uint16_t* src, float (&x)[8]) {
-  const uint4 q = reinterpret_cast<const uint4*>(src)[0];
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+template <bool NT, typename V>
+__device__ __forceinline__ void vstore(V* dst, V x) {
+  if constexpr (NT) __builtin_nontemporal_store(x, dst);
+  else *dst = x;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// V consecutive elements (V = 4 or 8) from a 16-byte-aligned f32 address.
+template <bool NT, int V>
+__device__ __forceinline__ void load_vec(const float* src, float (&x)[V]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int h = 0; h < V / 4; ++h) {
+    const f32x4 a = vload<NT>(reinterpret_cast<const f32x4*>(src) + h);
+    x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
+  }
+}
+
+// V consecutive bf16 elements (16 bytes for V = 8, 8 bytes for V = 4),
+// upcast exactly: the bf16 pattern is the high half of the f32 pattern.
+template <bool NT, int V>
+__device__ __forceinline__ void load_vec(const uint16_t* src, float (&x)[V]) {
+  uint32_t w[V / 2];
+  if constexpr (V == 8) {
+    const u32x4 q = vload<NT>(reinterpret_cast<const u32x4*>(src));
+    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+  } else {
+    static_assert(V == 4, "4 or 8 elements per lane");
+    const u32x2 q = vload<NT>(reinterpret_cast<const u32x2*>(src));
+    w[0] = q.x; w[1] = q.y;
+  }
+#pragma unroll
+  for (int k = 0; k < V / 2; ++k) {
     x[2 * k] = __uint_as_float(w[k] << 16);
     x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
   }
 }
 
-__device__ __forceinline__ void store8(float* dst, const float (&x)[8]) {
-  reinterpret_cast<float4*>(dst)[0] = make_float4(x[0], x[1], x[2], x[3]);
-  reinterpret_cast<float4*>(dst)[1] = make_float4(x[4], x[5], x[6], x[7]);
+template <bool NT, int V>
+__device__ __forceinline__ void store_vec(float* dst, const float (&x)[V]) {
+#pragma unroll
+  for (int h = 0; h < V / 4; ++h)
+    vstore<NT>(reinterpret_cast<f32x4*>(dst) + h,
+               f32x4{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]});
 }
 
-__device__ __forceinline__ void store8_bf16(uint16_t* dst, const uint32_t (&h)[8]) {
-  reinterpret_cast<uint4*>(dst)[0] =
-      make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                 h[6] | (h[7] << 16));
+template <bool NT, int V>
+__device__ __forceinline__ void store_vec_bf16(uint16_t* dst, const uint32_t (&h)[V]) {
+  if constexpr (V == 8) {
+    vstore<NT>(reinterpret_cast<u32x4*>(dst),
+               u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16)});
+  } else {
+    vstore<NT>(reinterpret_cast<u32x2*>(dst), u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+  }
 }
 
 // Element-wise forms for the ragged tail and for unaligned tensors: only
 // elements e < count are touched.
-__device__ __forceinline__ void load_n(const float* src, int count, float (&x)[8]) {
+template <int V>
+__device__ __forceinline__ void load_n(const float* src, int count, float (&x)[V]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (e < count) ? src[e] : 0.0f;
+  for (int e = 0; e < V; ++e) x[e] = (e < count) ? src[e] : 0.0f;
 }
 
-__device__ __forceinline__ void load_n(const uint16_t* src, int count, float (&x)[8]) {
+template <int V>
+__device__ __forceinline__ void load_n(const uint16_t* src, int count, float (&x)[V]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    x[e] = (e < count) ? bf16_bits_to_f32(src[e]) : 0.0f;
+  for (int e = 0; e < V; ++e) x[e] = (e < count) ? bf16_bits_to_f32(src[e]) : 0.0f;
 }
 
-__device__ __forceinline__ void store_n(float* dst, int count, const float (&x)[8]) {
+template <int V>
+__device__ __forceinline__ void store_n(float* dst, int count, const float (&x)[V]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int e = 0; e < V; ++e)
     if (e < count) dst[e] = x[e];
 }
 
-__device__ __forceinline__ void store_n_bf16(uint16_t* dst, int count,
-                                             const uint32_t (&h)[8]) {
+template <int V>
+__device__ __forceinline__ void store_n_bf16(uint16_t* dst, int count, const uint32_t (&h)[V]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int e = 0; e < V; ++e)
     if (e < count) dst[e] = static_cast<uint16_t>(h[e]);
 }
 

@@ -28,13 +28,14 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def workspace_bytes(n_tensors):
-    return _abi.asr_adamw_workspace_bytes(n_tensors)
+def workspace_bytes(numels):
+    """Workspace bytes for a list of tensors with these element counts."""
+    return _abi.asr_adamw_workspace_bytes([dict(numel=int(n)) for n in numels])
 
 
-def make_workspace(n_tensors, device):
-    """A device buffer big enough for a list of n_tensors."""
-    return torch.empty(max(workspace_bytes(n_tensors), 1), dtype=torch.uint8, device=device)
+def make_workspace(numels, device):
+    """A device buffer big enough for a list of tensors with these numels."""
+    return torch.empty(max(workspace_bytes(numels), 1), dtype=torch.uint8, device=device)
 
 
 def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1, beta2,
@@ -68,9 +69,9 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
         descs.append(_abi.AsrTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
                                     p.numel(), int(b) & 0xFFFFFFFFFFFFFFFF,
                                     _DTYPE_CODE[p.dtype], _DTYPE_CODE[g.dtype]))
-    need = workspace_bytes(n)
+    need = _abi.asr_adamw_workspace_bytes(descs)
     if workspace is None:
-        workspace = make_workspace(n, device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     if workspace.device != device or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must be on {device} and hold {need} bytes")
     with torch.cuda.device(device):

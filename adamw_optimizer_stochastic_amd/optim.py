@@ -68,10 +68,11 @@ class AdamWSR(torch.optim.Optimizer):
         """Global position of element 0 of parameter p."""
         return self._base_index[p]
 
-    def _workspace(self, device, n):
+    def _workspace(self, device, numels):
+        need = ops.workspace_bytes(numels)
         ws = self._workspaces.get(device)
-        if ws is None or ws.numel() < ops.workspace_bytes(n):
-            ws = ops.make_workspace(max(n, 64), device)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
             self._workspaces[device] = ws
         return ws
 
@@ -111,7 +112,7 @@ class AdamWSR(torch.optim.Optimizer):
                 ops.adamw_step(ps, gs, ms, vs, bases, lr=group["lr"], beta1=beta1, beta2=beta2,
                                eps=group["eps"], weight_decay=group["weight_decay"], step=t,
                                seed=self.seed, rounding=group["rounding"],
-                               workspace=self._workspace(device, len(ps)))
+                               workspace=self._workspace(device, [p.numel() for p in ps]))
         return loss
 
     def state_dict(self):
@@ -120,8 +121,24 @@ class AdamWSR(torch.optim.Optimizer):
         return sd
 
     def load_state_dict(self, state_dict):
+        """Like torch's, except that the moment states stay float32 whatever
+        the parameter dtype (torch's loader would cast them to it)."""
         extra = state_dict.get("adamw_sr")
-        state_dict = {k: v for k, v in state_dict.items() if k != "adamw_sr"}
-        super().load_state_dict(state_dict)
+        saved_state = state_dict.get("state", {})
+        plain = {k: v for k, v in state_dict.items() if k not in ("adamw_sr", "state")}
+        plain["state"] = {}
+        super().load_state_dict(plain)
+        saved_ids = [i for g in state_dict["param_groups"] for i in g["params"]]
+        params = [p for g in self.param_groups for p in g["params"]]
+        for pid, p in zip(saved_ids, params):
+            st = saved_state.get(pid)
+            if st is None:
+                continue
+            self.state[p] = {
+                "step": torch.as_tensor(st["step"], dtype=torch.float32).detach().clone().cpu(),
+                "exp_avg": st["exp_avg"].detach().to(device=p.device, dtype=torch.float32).clone(),
+                "exp_avg_sq": st["exp_avg_sq"].detach().to(device=p.device,
+                                                            dtype=torch.float32).clone(),
+            }
         if extra is not None:
             self.seed = int(extra["seed"])

@@ -105,7 +105,7 @@ def run_adamw(args, torch, ops, wl):
     lists = ([t["param"] for t in state], [t["grad"] for t in state],
              [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
              [t["base_index"] for t in state])
-    ws = ops.make_workspace(len(state), dev)
+    ws = ops.make_workspace([t["param"].numel() for t in state], dev)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0,
               rounding="sr", workspace=ws)
     torch.cuda.synchronize()
@@ -142,10 +142,11 @@ def run_adamw(args, torch, ops, wl):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "adamw_sr_multi_tensor<BF16,BF16,SR>",
+                     "kernel": "adamw_sr_class<BF16,BF16,SR> (one launch per size class) + "
+                               "adamw_sr_slots<BF16,BF16,SR> (small tensors)",
                      "kernel_ms_avg": kernel_ms,
-                     "timing": "HIP events on the launch stream around each step call "
-                               "(includes its metadata upload launches)"},
+                     "timing": "HIP events on the launch stream around each step call: all "
+                               "kernels of one step (metadata upload, slot table, step)"},
     }
 
 

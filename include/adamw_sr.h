@@ -79,9 +79,12 @@ typedef struct asr_tensor {
   int32_t grad_dtype;   /* ASR_F32 | ASR_BF16                                */
 } asr_tensor;
 
-/* Bytes of device workspace asr_adamw_step needs for a list of n_tensors
- * (0 for n_tensors <= 0). The workspace holds the list's metadata table. */
-size_t asr_adamw_workspace_bytes(int32_t n_tensors);
+/* Bytes of device workspace asr_adamw_step needs for this list (0 when
+ * n_tensors <= 0 or tensors is NULL). Only the count of tensors and their
+ * numel matter, so the size stays valid across steps of a fixed list. The
+ * workspace holds the list's metadata and a table of one 32-bit entry per
+ * 1,024-element slot (under 0.4% of the bf16 parameter bytes). */
+size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors);
 
 /*
  * One AdamW step over a list of tensors, in one pass over memory.
@@ -109,14 +112,14 @@ size_t asr_adamw_workspace_bytes(int32_t n_tensors);
  * step         1-based step count t, in [1, 2**32 - 1]; used for the bias
  *              corrections and as key word 1.
  * seed         key word 0.
- * workspace    device buffer of at least asr_adamw_workspace_bytes(n_tensors)
- *              bytes, 16-byte aligned, owned by the caller. Its contents are
- *              overwritten (stream-ordered); it must not be used by other
- *              work that runs concurrently with this step.
+ * workspace    device buffer of at least asr_adamw_workspace_bytes(tensors,
+ *              n_tensors) bytes, 16-byte aligned, owned by the caller. Its
+ *              contents are overwritten (stream-ordered); it must not be used
+ *              by other work that runs concurrently with this step.
  * Errors: ASR_EINVAL (n_tensors < 0, NULL tensors with n_tensors > 0,
  * numel < 0, a NULL buffer in a non-empty tensor, hyperparameter or step out
- * of range, rounding code unknown, more than 2**47 elements of one dtype
- * pair), ASR_EDTYPE, ASR_EALIGN (param/grad not aligned to 2 or 4 bytes as
+ * of range, rounding code unknown, more than 2**32 slots of 1,024 elements
+ * of one dtype pair), ASR_EDTYPE, ASR_EALIGN (param/grad not aligned to 2 or 4 bytes as
  * their dtype needs, m/v not 4-byte aligned), ASR_EWORKSPACE, ASR_EHIP.
  * Tensors whose four buffers are 16-byte aligned take the 128-bit path;
  * others are processed element by element with identical results.

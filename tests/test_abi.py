@@ -52,13 +52,18 @@ def test_struct_layout():
 
 
 def test_workspace_bytes():
-    assert _abi.asr_adamw_workspace_bytes(0) == 0
-    assert _abi.asr_adamw_workspace_bytes(-3) == 0
+    assert _abi.asr_adamw_workspace_bytes([]) == 0
     prev = 0
     for n in [1, 2, 7, 64, 291, 5000]:
-        b = _abi.asr_adamw_workspace_bytes(n)
-        assert b >= 56 * n + 4 * (n + 1) and b % 256 == 0 and b >= prev
+        numels = [(k * 7919) % 100000 + 1 for k in range(n)]
+        b = _abi.asr_adamw_workspace_bytes([dict(numel=x) for x in numels])
+        slots = sum((x + 2047) // 2048 for x in numels)
+        assert b >= 56 * n + 4 * n + 4 * slots and b % 256 == 0 and b >= prev
         prev = b
+    # empty tensors take no slots; the size depends only on count and numel
+    a = _abi.asr_adamw_workspace_bytes([dict(numel=0), dict(numel=4096)])
+    b = _abi.asr_adamw_workspace_bytes([dict(numel=0, param=8, base_index=5), dict(numel=4096)])
+    assert a == b > 0
 
 
 @pytest.mark.parametrize("lr,b1,b2,eps,wd", [

@@ -218,7 +218,7 @@ def test_subulp_accumulation_full_size():
         w = torch.full((n,), 1.0, dtype=torch.bfloat16, device="cuda")
         m = torch.zeros(n, dtype=torch.float32, device="cuda")
         v = torch.zeros(n, dtype=torch.float32, device="cuda")
-        ws = ops.make_workspace(1, "cuda")
+        ws = ops.make_workspace([n], "cuda")
         for t in range(1, T + 1):
             g = w.float() - 1.5                       # exact in binary32
             ops.adamw_step([w], [g], [m], [v], [0], lr=lr, beta1=0.9, beta2=0.999, eps=1e-8,
@@ -281,7 +281,7 @@ def test_optimizer_class_matches_oracle_and_resumes():
                                                   step=steps[k], seed=5, **HP)
     for k, p in enumerate(params):
         assert_bits_equal(wl.tensor_to_bf16_bits(p.detach().reshape(-1)), host[k][0], f"param {k}")
-        assert_bits_equal(to_host(opt.state[p]["exp_avg"]), host[k][1], f"m {k}")
+        assert_bits_equal(to_host(opt.state[p]["exp_avg"]).reshape(-1), host[k][1], f"m {k}")
     # Resume: a fresh optimizer loaded from the state dict continues identically.
     sd = opt.state_dict()
     clone = torch.nn.Sequential(torch.nn.Linear(64, 96), torch.nn.ReLU(),
@@ -306,3 +306,31 @@ def test_optimizer_rejects_unsupported_options():
         AdamWSR([torch.zeros(4, device="cuda", dtype=torch.float16, requires_grad=True)])
     with pytest.raises(ValueError):
         AdamWSR([torch.zeros(4, device="cuda", requires_grad=True)], seed=1 << 32)
+
+
+def test_size_classes_and_leftovers_in_one_call():
+    """Equal-size tensors (ragged numel) large enough to be launched as a size
+    class, one of them an unaligned view, plus small tensors of distinct
+    sizes that go through the slot table, all in one call, with odd base
+    indices. Every element against the oracle."""
+    announce("size classes + leftovers")
+    rng = wl.host_rng(wl.CFG_SMALL, 77, 0)
+    specs = [110001] * 40 + [2500003] * 2 + [1, 9, 4097, 65536 + 5]
+    host, dev, bases, base = [], [], [], 3
+    for k, n in enumerate(specs):
+        off = 1 if k == 7 else 0          # one unaligned view inside the class
+        p = _host_tensor(rng, n + off, BF16, 0.02)
+        g = _host_tensor(rng, n + off, BF16, 1e-3)
+        m = wl.normal_f32(rng, n + off, 1e-4)
+        v = np.abs(wl.normal_f32(rng, n + off, 1e-7))
+        host.append((p[off:], g[off:], m[off:], v[off:]))
+        dev.append((bf16_tensor(p)[off:], bf16_tensor(g)[off:], f32_tensor(m)[off:],
+                    f32_tensor(v)[off:]))
+        bases.append(base)
+        base += n + (k % 3)               # gaps: positions need not be dense
+    ops.adamw_step([d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev],
+                   [d[3] for d in dev], bases, step=6, seed=12, **HP)
+    for k, ((p, g, m, v), d, b) in enumerate(zip(host, dev, bases)):
+        want = oracle.step_tensor(p, g, m, v, param_dtype=BF16, grad_dtype=BF16, base_index=b,
+                                  step=6, seed=12, **HP)
+        _check_outputs((d[0], d[2], d[3]), want, BF16, f"tensor {k} (n={specs[k]})")

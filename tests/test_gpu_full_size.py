@@ -143,7 +143,7 @@ def test_llama3_8b_list_two_steps_sampled():
         for s in starts:
             e = min(n, s + (n if n <= 3 * win else win))
             samples.append((t, s, e, to_host(t["param"][s:e]), to_host(t["grad"][s:e])))
-    ws = ops.make_workspace(len(state), dev)
+    ws = ops.make_workspace([t["param"].numel() for t in state], dev)
     lists = ([t["param"] for t in state], [t["grad"] for t in state],
              [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
              [t["base_index"] for t in state])

@@ -1,0 +1,61 @@
+"""Host logic of the AdamWSR optimizer (CPU only; no kernel runs here):
+global positions (base_index) as running numel in parameter order, rejected
+options, and a state_dict round trip that keeps the f32 moment states f32
+for bf16 parameters (torch's loader would cast them to the param dtype)."""
+
+import pytest
+import torch
+
+from adamw_optimizer_stochastic_amd import AdamWSR
+
+
+def test_base_index_is_running_numel_in_group_order():
+    a = torch.nn.Parameter(torch.zeros(3, 5))
+    b = torch.nn.Parameter(torch.zeros(7))
+    c = torch.nn.Parameter(torch.zeros(2, 2))
+    opt = AdamWSR([{"params": [a, b]}, {"params": [c], "lr": 1e-4}])
+    assert [opt.base_index(p) for p in (a, b, c)] == [0, 15, 22]
+    d = torch.nn.Parameter(torch.zeros(11))
+    opt.add_param_group({"params": [d]})
+    assert opt.base_index(d) == 26 and opt.base_index(a) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(amsgrad=True), dict(maximize=True), dict(foreach=True),
+                                dict(fused=True), dict(capturable=True)])
+def test_unsupported_options_raise(kw):
+    with pytest.raises(NotImplementedError):
+        AdamWSR([torch.nn.Parameter(torch.zeros(4))], **kw)
+
+
+@pytest.mark.parametrize("kw", [dict(lr=-1.0), dict(eps=-1e-8), dict(betas=(1.0, 0.9)),
+                                dict(weight_decay=-0.1), dict(seed=-1), dict(seed=1 << 32),
+                                dict(rounding="rz")])
+def test_bad_values_raise(kw):
+    with pytest.raises(ValueError):
+        AdamWSR([torch.nn.Parameter(torch.zeros(4))], **kw)
+
+
+def test_unsupported_param_dtypes():
+    for dt in (torch.float16, torch.float64, torch.complex64):
+        with pytest.raises(NotImplementedError):
+            AdamWSR([torch.nn.Parameter(torch.zeros(4, dtype=dt))])
+
+
+def test_state_dict_round_trip_keeps_f32_states():
+    m = torch.nn.Linear(4, 3).to(torch.bfloat16)
+    opt = AdamWSR(m.parameters(), seed=9, weight_decay=0.05)
+    torch.manual_seed(0)
+    for p in m.parameters():
+        opt.state[p] = {"step": torch.tensor(3.0), "exp_avg": torch.randn(p.shape),
+                        "exp_avg_sq": torch.rand(p.shape)}
+    sd = opt.state_dict()
+    m2 = torch.nn.Linear(4, 3).to(torch.bfloat16)
+    opt2 = AdamWSR(m2.parameters())
+    opt2.load_state_dict(sd)
+    assert opt2.seed == 9 and opt2.param_groups[0]["weight_decay"] == 0.05
+    for p2, p in zip(m2.parameters(), m.parameters()):
+        s2, s = opt2.state[p2], opt.state[p]
+        assert s2["exp_avg"].dtype == torch.float32
+        assert torch.equal(s2["exp_avg"], s["exp_avg"])
+        assert torch.equal(s2["exp_avg_sq"], s["exp_avg_sq"])
+        assert float(s2["step"]) == 3.0
