@@ -7,7 +7,8 @@
 //     unbiased bf16 write-back, no fp32 master), Usage (drop-in for
 //     torch.optim.AdamW; f32 states; f32|bf16 params and grads), Method
 //     (Philox keyed by (seed, step), indexed by global element position),
-//     Correctness (per-shard base_index equals the whole update bitwise).
+//     Correctness (shards that pass their own base_index reproduce the
+//     one-piece update bit for bit).
 //   "Add stochastic rounding and philox RNG helpers" (FlyDSL pull request):
 //     Primitives (Philox words, add-and-truncate SR), discussion (SR as a
 //     rounding mode of the f32 -> bf16 conversion).

@@ -3,11 +3,11 @@
 From the "adamw-sr" page (Usage section): a drop-in for torch.optim.AdamW
 taking lr, weight_decay and seed; optimizer states are float32; parameters
 and gradients may be f32 or bf16; stochastic rounding is on by default for
-bf16 parameters. The Method section indexes the randomness by each
-element's global parameter position; reading: the position of a tensor's
-first element is the running total of numel over all parameters of the
-optimizer, in param_groups order and then parameter order, fixed when the
-parameter is added (later groups are appended after it).
+bf16 parameters. The Method section derives the random bits from each
+element's position in the whole parameter set; reading: the position of a
+tensor's first element is the running total of numel over all parameters
+of the optimizer, in param_groups order and then parameter order, fixed
+when the parameter is added (later groups are appended after it).
 
 Unsupported AdamW options raise NotImplementedError rather than silently
 computing something else.

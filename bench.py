@@ -17,6 +17,7 @@ import hashlib
 import json
 import multiprocessing
 import os
+import re
 import sys
 import time
 
@@ -31,10 +32,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f
 
 
 def source_hash():
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
+    so editing a comment keeps counter data valid and any code change voids it."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -6,10 +6,11 @@
  *   - "adamw-sr" (kernels hub page), intro, Usage, Method, Correctness:
  *     a decoupled-weight-decay Adam step with float32 moment states, f32 or
  *     bf16 parameters and gradients, bf16 parameters written back by
- *     unbiased stochastic rounding with no fp32 master copy, randomness from
- *     counter-based Philox keyed by (seed, step) and indexed by each
- *     element's global parameter position, so whole and sharded updates
- *     agree bit for bit when each shard passes its own base_index;
+ *     unbiased stochastic rounding with no fp32 master copy; the random bits
+ *     come from a counter-based Philox whose key is the pair (seed, step)
+ *     and whose counter is derived from the element's position in the whole
+ *     parameter set, so a tensor updated in one piece or in shards (each
+ *     shard passing the position of its first element) gets the same bits;
  *   - "Add stochastic rounding and philox RNG helpers" (FlyDSL pull request),
  *     Primitives: philox_4x32(counter, key) -> four 32-bit words, and
  *     stochastic rounding f32 -> bf16 by adding 16 random bits to the 16

@@ -12,8 +12,8 @@ Sources (the pages are cited by title and section):
     counter-based Philox generator.
   * "adamw-sr" (kernels hub page), intro, Usage, Method, Correctness sections:
     the decoupled-weight-decay AdamW step, fp32 states, bf16 write-back by
-    stochastic rounding, randomness keyed by (seed, step) and indexed by the
-    global element position.
+    stochastic rounding, random bits tied to the key (seed, step) and to
+    each element's position in the whole parameter set.
   * Published definitions the pages name but do not print: Philox4x32 with 10
     rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
     1, 2, 3", SC 2011) and the AdamW update as documented for

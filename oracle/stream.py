@@ -1,10 +1,10 @@
 """Which 16 random bits each element receives (the stream contract).
 
-The "adamw-sr" page (Method section) keys the rounding randomness by
-(seed, step) and indexes it by each element's global parameter position, so
-that a parameter updated whole, or in shards that each carry the global
-position of their first element (Correctness section: per-shard
-base_index), gets the same bits. The FlyDSL page's device tests feed one
+The "adamw-sr" page (Method section) takes the rounding randomness from a
+key made of (seed, step) and from each element's position in the whole
+parameter set; its Correctness section states that a parameter updated in
+shards, each carrying the position of its first element (base_index),
+receives the same bits as when updated in one piece. The FlyDSL page's device tests feed one
 Philox word per element, indexed by the global thread index, with the seed
 as key.
 

@@ -2,7 +2,7 @@
   * the SR conversion of 2**30 f32 values with 0.1% +-Inf/NaN/FLT_MAX;
   * a 268,435,456-element bf16 step run whole, as 8 shards with their own
     base_index, and split at an odd element (adamw-sr page, Correctness:
-    per-shard base_index equals the whole update bitwise);
+    sharded and one-piece updates must agree bit for bit);
   * one multi-tensor call over the whole Llama-3-8B-shaped list.
 Outputs are checked bit for bit against the oracle on sampled windows and
 special positions, and by properties that hold at any size on the rest.

@@ -1,9 +1,9 @@
 """Pins of the oracle's f32 -> bf16 conversions (CPU only).
 
 What pins them:
-  * the exact-unbiasedness identity of the FlyDSL page's Tests section: over
-    all 65,536 random values, the number of round-ups equals the discarded
-    low 16 bits (brute force);
+  * the exact-unbiasedness identity of the FlyDSL page's Tests section: the
+    count of random values (out of 65,536) that carry into the kept half is
+    the dropped low half read as an integer (brute force);
   * outputs land only on the two bf16 neighbours, checked by comparing real
     values (not bit patterns);
   * random value 0 gives round-toward-zero and 0xFFFF round-away-from-zero
