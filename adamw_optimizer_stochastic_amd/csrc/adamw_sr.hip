@@ -43,7 +43,15 @@ constexpr int kBlock = 256;            // 4 waves of 64 lanes
 #define ASR_VEC 4
 #endif
 constexpr int kVec = ASR_VEC;          // elements per lane of the step kernel
-constexpr int kCvtVec = 8;             // elements per lane of the converts
+#ifndef ASR_CVT_VEC
+#define ASR_CVT_VEC 8
+#endif
+constexpr int kCvtVec = ASR_CVT_VEC;   // elements per lane of the converts
+constexpr int64_t kCvtSlot = kBlock * kCvtVec;
+#ifndef ASR_CVT_BLOCKS_PER_CU
+#define ASR_CVT_BLOCKS_PER_CU 4
+#endif
+constexpr int kCvtBlocksPerCU = ASR_CVT_BLOCKS_PER_CU;
 constexpr int64_t kSlot = kBlock * kVec;  // elements per workgroup of the step kernel
 // Blocks per launch; a larger list is covered by several launches.
 constexpr uint32_t kMaxGrid = 1u << 23;
@@ -244,60 +252,59 @@ philox_fill(uint32_t* __restrict__ out, int64_t n_counters, uint64_t counter_bas
 }
 
 // ------------------------------------------------------ f32 -> bf16 converts
+// One lane's kCvtVec elements i0 .. of the conversion (count inside: 0..V).
 template <int ROUND, int PHASE, bool VEC>
-__device__ __forceinline__ void convert_all(const float* __restrict__ in,
-                                            uint16_t* __restrict__ out, int64_t n,
-                                            uint64_t base_index, uint32_t seed,
-                                            uint32_t step) {
+__device__ __forceinline__ void convert_run(const float* __restrict__ in,
+                                            uint16_t* __restrict__ out, int64_t i0, int count,
+                                            uint64_t base_index, uint32_t seed, uint32_t step) {
   constexpr int V = kCvtVec;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock * V;
-  for (int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * V; i0 < n;
-       i0 += stride) {
-    const int64_t left = n - i0;
-    const int count = left < V ? static_cast<int>(left) : V;
-    const bool full = VEC && count == V;
-    float x[V];
-    if (full) load_vec<kNonTemporal, V>(in + i0, x);
-    else load_n(in + i0, count, x);
-    uint32_t h[V];
-    if constexpr (ROUND == kRoundSR) {
-      uint32_t r[V];
-      stream_bits<PHASE, V>(base_index + static_cast<uint64_t>(i0), seed, step, r);
+  const bool full = VEC && count == V;
+  float x[V];
+  if (full) load_vec<kNonTemporal, V>(in + i0, x);
+  else load_n(in + i0, count, x);
+  uint32_t h[V];
+  if constexpr (ROUND == kRoundSR) {
+    uint32_t r[V];
+    stream_bits<PHASE, V>(base_index + static_cast<uint64_t>(i0), seed, step, r);
 #pragma unroll
-      for (int e = 0; e < V; ++e) h[e] = round_sr(__float_as_uint(x[e]), r[e]);
-    } else {
+    for (int e = 0; e < V; ++e) h[e] = round_sr(__float_as_uint(x[e]), r[e]);
+  } else {
 #pragma unroll
-      for (int e = 0; e < V; ++e) h[e] = round_rn(__float_as_uint(x[e]));
-    }
-    if (full) store_vec_bf16<kNonTemporal, V>(out + i0, h);
-    else store_n_bf16(out + i0, count, h);
+    for (int e = 0; e < V; ++e) h[e] = round_rn(__float_as_uint(x[e]));
   }
+  if (full) store_vec_bf16<kNonTemporal, V>(out + i0, h);
+  else store_n_bf16(out + i0, count, h);
 }
 
+// One slot of kCvtSlot elements per workgroup, no loop (as for the step).
 template <int ROUND>
 __global__ void __launch_bounds__(kBlock)
 convert_f32_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n,
-                 uint64_t base_index, uint32_t seed, uint32_t step, int vec_ok) {
+                 uint64_t slot0, uint64_t base_index, uint32_t seed, uint32_t step, int vec_ok) {
+  const int64_t i0 = static_cast<int64_t>(slot0 + blockIdx.x) * kCvtSlot +
+                     static_cast<int64_t>(threadIdx.x) * kCvtVec;
+  const int64_t left = n - i0;
+  const int count = left <= 0 ? 0 : (left < kCvtVec ? static_cast<int>(left) : kCvtVec);
   if constexpr (ROUND == kRoundSR) {
     const int phase = static_cast<int>(base_index & 3u);
     if (vec_ok) {
       switch (phase) {
-        case 0: convert_all<ROUND, 0, true>(in, out, n, base_index, seed, step); break;
-        case 1: convert_all<ROUND, 1, true>(in, out, n, base_index, seed, step); break;
-        case 2: convert_all<ROUND, 2, true>(in, out, n, base_index, seed, step); break;
-        default: convert_all<ROUND, 3, true>(in, out, n, base_index, seed, step); break;
+        case 0: convert_run<ROUND, 0, true>(in, out, i0, count, base_index, seed, step); break;
+        case 1: convert_run<ROUND, 1, true>(in, out, i0, count, base_index, seed, step); break;
+        case 2: convert_run<ROUND, 2, true>(in, out, i0, count, base_index, seed, step); break;
+        default: convert_run<ROUND, 3, true>(in, out, i0, count, base_index, seed, step); break;
       }
     } else {
       switch (phase) {
-        case 0: convert_all<ROUND, 0, false>(in, out, n, base_index, seed, step); break;
-        case 1: convert_all<ROUND, 1, false>(in, out, n, base_index, seed, step); break;
-        case 2: convert_all<ROUND, 2, false>(in, out, n, base_index, seed, step); break;
-        default: convert_all<ROUND, 3, false>(in, out, n, base_index, seed, step); break;
+        case 0: convert_run<ROUND, 0, false>(in, out, i0, count, base_index, seed, step); break;
+        case 1: convert_run<ROUND, 1, false>(in, out, i0, count, base_index, seed, step); break;
+        case 2: convert_run<ROUND, 2, false>(in, out, i0, count, base_index, seed, step); break;
+        default: convert_run<ROUND, 3, false>(in, out, i0, count, base_index, seed, step); break;
       }
     }
   } else {
-    if (vec_ok) convert_all<ROUND, 0, true>(in, out, n, base_index, seed, step);
-    else convert_all<ROUND, 0, false>(in, out, n, base_index, seed, step);
+    if (vec_ok) convert_run<ROUND, 0, true>(in, out, i0, count, base_index, seed, step);
+    else convert_run<ROUND, 0, false>(in, out, i0, count, base_index, seed, step);
   }
 }
 
@@ -717,17 +724,28 @@ static int convert(int rounding, const float* in, uint16_t* out, int64_t n, uint
   if (!aligned(in, 4) || !aligned(out, 2))
     return fail(ASR_EALIGN, "buffer not aligned to its element size");
   if (n > (int64_t{1} << 62)) return fail(ASR_EINVAL, "n too large");
-  const int64_t blocks = (n + asr::kBlock * asr::kCvtVec - 1) / (asr::kBlock * asr::kCvtVec);
-  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(blocks, 1 << 16));
+  const uint64_t n_slots = (static_cast<uint64_t>(n) + asr::kCvtSlot - 1) / asr::kCvtSlot;
   const int vec_ok = aligned(in, 16) && aligned(out, 16);
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  hipError_t e =
-      rounding == ASR_ROUND_SR
-          ? launch(asr::convert_f32_bf16<asr::kRoundSR>, grid, stream, in, out, n, base_index,
-                   seed, step, vec_ok)
-          : launch(asr::convert_f32_bf16<asr::kRoundRN>, grid, stream, in, out, n, base_index,
-                   seed, step, vec_ok);
-  if (e != hipSuccess) return hip_fail(e, "convert launch");
+  using K = void (*)(const float*, uint16_t*, int64_t, uint64_t, uint64_t, uint32_t, uint32_t, int);
+  const K k = rounding == ASR_ROUND_SR ? asr::convert_f32_bf16<asr::kRoundSR>
+                                       : asr::convert_f32_bf16<asr::kRoundRN>;
+  uint32_t lds = 0;
+  if (asr::kCvtBlocksPerCU > 0) {
+    lds = (asr::kLdsPerCU / asr::kCvtBlocksPerCU) & ~1023u;
+    if (lds > 64u * 1024u) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return hip_fail(e, "convert attribute");
+    }
+  }
+  for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
+    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
+    hipError_t e = launch_lds(k, grid, lds, stream, in, out, n, slot0, base_index, seed, step,
+                              vec_ok);
+    if (e != hipSuccess) return hip_fail(e, "convert launch");
+  }
   return ok();
 }
 

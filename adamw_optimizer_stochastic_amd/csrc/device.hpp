@@ -44,8 +44,9 @@ __device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1,
   for (int round = 0; round < 10; ++round) {
     const uint64_t prod_a = static_cast<uint64_t>(c0) * kPhiloxMulA;
     const uint64_t prod_b = static_cast<uint64_t>(c2) * kPhiloxMulB;
-    const uint32_t next0 = static_cast<uint32_t>(prod_b >> 32) ^ c1 ^ k0;
-    const uint32_t next2 = static_cast<uint32_t>(prod_a >> 32) ^ c3 ^ k1;
+    // three-input XOR in one gfx950 instruction (truth table 0x96 = a^b^c)
+    const uint32_t next0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(prod_b >> 32), c1, k0, 0x96);
+    const uint32_t next2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(prod_a >> 32), c3, k1, 0x96);
     c1 = static_cast<uint32_t>(prod_b);
     c3 = static_cast<uint32_t>(prod_a);
     c0 = next0;
