@@ -49,7 +49,7 @@ constexpr int kVec = ASR_VEC;          // elements per lane of the step kernel
 constexpr int kCvtVec = ASR_CVT_VEC;   // elements per lane of the converts
 constexpr int64_t kCvtSlot = kBlock * kCvtVec;
 #ifndef ASR_CVT_BLOCKS_PER_CU
-#define ASR_CVT_BLOCKS_PER_CU 4
+#define ASR_CVT_BLOCKS_PER_CU 6
 #endif
 constexpr int kCvtBlocksPerCU = ASR_CVT_BLOCKS_PER_CU;
 constexpr int64_t kSlot = kBlock * kVec;  // elements per workgroup of the step kernel
@@ -300,9 +300,11 @@ __device__ __forceinline__ void convert_run(const float* __restrict__ in,
 }
 
 #ifndef ASR_CVT_WINDOWS
-#define ASR_CVT_WINDOWS 1
+#define ASR_CVT_WINDOWS 8
 #endif
-// The conversion has two streams only; one window measured best for it.
+// One window per XCD and six resident workgroups per CU measured best for
+// the conversion (6.13-6.15 TB/s on 2**30 elements against 5.74-6.06 for
+// one window at four to eight workgroups).
 constexpr uint32_t kCvtWindows = ASR_CVT_WINDOWS;
 __device__ __forceinline__ uint32_t cvt_slot_of_block(uint32_t b, uint32_t grid) {
   if constexpr (kCvtWindows > 1) {
