@@ -334,3 +334,38 @@ def test_size_classes_and_leftovers_in_one_call():
         want = oracle.step_tensor(p, g, m, v, param_dtype=BF16, grad_dtype=BF16, base_index=b,
                                   step=6, seed=12, **HP)
         _check_outputs((d[0], d[2], d[3]), want, BF16, f"tensor {k} (n={specs[k]})")
+
+
+@pytest.mark.parametrize("hp", [
+    dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1),
+    dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0, step=1),
+    dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=0.0, weight_decay=0.01, step=1),
+    dict(lr=1e-3, beta1=0.9, beta2=0.99999, eps=1e-8, weight_decay=0.01, step=1),
+    dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=2**32 - 1),
+    dict(lr=5.0, beta1=0.5, beta2=0.5, eps=1e-3, weight_decay=0.19, step=7),
+])
+def test_degenerate_hyperparameters(hp):
+    """Corner values of the hyperparameters: lr 0 (parameters keep their
+    value), betas 0 (m = g, v = g*g), eps 0 with zero moments and zero
+    gradients (0/0 gives NaN on both sides), beta2 near 1, the largest step,
+    a large lr. Bit-exact against the oracle (NaN-ness where a NaN forms)."""
+    announce("degenerate hp", hp)
+    rng = wl.host_rng(wl.CFG_SMALL, 500, int(hp["step"]) % 1000)
+    n = 5000
+    for pdt in (F32, BF16):
+        p = _host_tensor(rng, n, pdt, 0.02)
+        g = wl.normal_f32(rng, n, 1e-3)
+        m = wl.normal_f32(rng, n, 1e-4)
+        v = np.abs(wl.normal_f32(rng, n, 1e-7))
+        g[:7] = 0.0
+        m[:7] = 0.0
+        v[:7] = 0.0
+        pd, gd, md, vd = _to_dev(p, pdt), f32_tensor(g), f32_tensor(m), f32_tensor(v)
+        kw = dict(lr=hp["lr"], beta1=hp["beta1"], beta2=hp["beta2"], eps=hp["eps"],
+                  weight_decay=hp["weight_decay"])
+        ops.adamw_step([pd], [gd], [md], [vd], [11], step=hp["step"], seed=4, **kw)
+        want = oracle.step_tensor(p, g, m, v, param_dtype=pdt, grad_dtype=F32, base_index=11,
+                                  step=hp["step"], seed=4, **kw)
+        _check_outputs((pd, md, vd), want, pdt, f"pdt={pdt}", nan_ok=True)
+        if hp["lr"] == 0.0:
+            assert_bits_equal(to_host(pd), p, "lr = 0 keeps the parameters")

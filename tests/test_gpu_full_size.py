@@ -164,3 +164,65 @@ def test_llama3_8b_list_two_steps_sampled():
         assert_bits_equal(to_host(t["exp_avg"][s:e]), m, what + " m")
         assert_bits_equal(to_host(t["exp_avg_sq"][s:e]), v, what + " v")
     del state, lists
+
+
+def test_tensors_beyond_2pow32_elements_and_two_launches():
+    """Two equal tensors of 4,400,000,037 bf16 elements each: element offsets
+    past 2**32 inside one tensor, and more slots than one launch covers, so
+    the size class is split over two launches. Windows around element 2**32,
+    around the launch boundary, at both ends of each tensor, against the
+    oracle; base indices with an odd phase."""
+    n = 4_400_000_037
+    dev = torch.device("cuda", 0)
+    announce("beyond 2**32: inputs (106 GB)")
+    gen = wl.device_generator(dev, wl.CFG_SHARDS, 77)
+    ts = []
+    for k in range(2):
+        p = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        g = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        for s in range(0, n, 1 << 30):                     # bounded temporaries
+            e = min(n, s + (1 << 30))
+            p[s:e] = wl.device_normal(e - s, 0.02, gen, dev, torch.bfloat16)
+            g[s:e] = wl.device_normal(e - s, 1e-3, gen, dev, torch.bfloat16)
+        ts.append(dict(p=p, g=g, m=torch.zeros(n, dtype=torch.float32, device=dev),
+                       v=torch.zeros(n, dtype=torch.float32, device=dev)))
+    base0 = (1 << 40) + 3
+    bases = [base0, base0 + n]
+    slot = 1024                                             # elements per slot
+    per = -(-n // slot)                                     # slots per tensor
+    second = (1 << 23) - per                                # launch boundary in tensor 1
+    w = 4096
+    wins = [(0, 0), (0, (1 << 32) - w // 2), (0, n - w - 5), (1, 0),
+            (1, second * slot - w // 2), (1, (1 << 32) - w // 2), (1, n - w)]
+    host = [(k, s, to_host(ts[k]["p"][s:s + w]), to_host(ts[k]["g"][s:s + w])) for k, s in wins]
+    announce("beyond 2**32: step")
+    ops.adamw_step([t["p"] for t in ts], [t["g"] for t in ts], [t["m"] for t in ts],
+                   [t["v"] for t in ts], bases, step=3, seed=21, **HP)
+    torch.cuda.synchronize()
+    z = np.zeros(w, np.float32)
+    for k, s, hp_, hg in host:
+        want = oracle.step_tensor(hp_, hg, z, z, param_dtype=BF16, grad_dtype=BF16,
+                                  base_index=bases[k] + s, step=3, seed=21, **HP)
+        what = f"tensor {k} [{s}:{s + w}]"
+        assert_bits_equal(to_host(ts[k]["p"][s:s + w]), want[0], what + " param")
+        assert_bits_equal(to_host(ts[k]["m"][s:s + w]), want[1], what + " m")
+        assert_bits_equal(to_host(ts[k]["v"][s:s + w]), want[2], what + " v")
+    del ts
+
+
+def test_convert_beyond_2pow32_elements():
+    n = (1 << 32) + 4099
+    dev = torch.device("cuda", 0)
+    announce("convert beyond 2**32: inputs")
+    gen = wl.device_generator(dev, wl.CFG_CONVERT, 9)
+    x = torch.empty(n, dtype=torch.float32, device=dev)
+    for s in range(0, n, 1 << 30):
+        e = min(n, s + (1 << 30))
+        x[s:e] = wl.device_normal(e - s, 1.0, gen, dev, torch.float32)
+    base = (1 << 33) + 1
+    out = ops.cvt_f32_bf16_sr(x, 5, 11, base)
+    torch.cuda.synchronize()
+    for s in (0, (1 << 31) - 100, (1 << 32) - 3000, n - 5000):
+        xs = to_host(x[s:s + 5000])
+        assert_bits_equal(to_host(out[s:s + 5000]), oracle.cvt_f32_bf16_sr(xs, 5, 11, base + s),
+                          f"window {s}")
