@@ -58,6 +58,7 @@ _SIGNATURES = {
                                        _c.c_uint32, _c.c_uint64, _c.c_void_p]),
     "asr_cvt_f32_bf16_rn": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "asr_f32_sqrt_div": (_c.c_int, [_c.c_void_p] * 4 + [_c.c_int64, _c.c_void_p]),
+    "asr_sr_bf16_given_bits": (_c.c_int, [_c.c_void_p] * 3 + [_c.c_int64, _c.c_void_p]),
 }
 
 _lock = threading.Lock()
@@ -146,3 +147,7 @@ def asr_cvt_f32_bf16_rn(inp, out, n, stream):
 
 def asr_f32_sqrt_div(a, b, sqrt_out, div_out, n, stream):
     _check(lib().asr_f32_sqrt_div(a, b, sqrt_out, div_out, n, stream), "asr_f32_sqrt_div")
+
+
+def asr_sr_bf16_given_bits(x, r16, out, n, stream):
+    _check(lib().asr_sr_bf16_given_bits(x, r16, out, n, stream), "asr_sr_bf16_given_bits")

@@ -349,6 +349,16 @@ convert_f32_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64
   }
 }
 
+// ---------------------------------------------- SR with caller's bits
+// out[i] = SR(x[i], r16[i]): the rounding with its random bits supplied.
+__global__ void __launch_bounds__(kBlock)
+sr_given_bits(const float* __restrict__ x, const uint16_t* __restrict__ r16,
+              uint16_t* __restrict__ out, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride)
+    out[i] = static_cast<uint16_t>(round_sr(__float_as_uint(x[i]), r16[i]));
+}
+
 // ------------------------------------------------ sqrt / division probe
 __global__ void __launch_bounds__(kBlock)
 sqrt_div(const float* __restrict__ a, const float* __restrict__ b,
@@ -797,6 +807,21 @@ int asr_cvt_f32_bf16_sr(const float* in, uint16_t* out, int64_t n, uint32_t seed
 
 int asr_cvt_f32_bf16_rn(const float* in, uint16_t* out, int64_t n, void* stream) {
   return convert(ASR_ROUND_RN, in, out, n, 0, 0, 0, stream);
+}
+
+int asr_sr_bf16_given_bits(const float* x, const uint16_t* r16, uint16_t* out, int64_t n,
+                           void* stream_ptr) {
+  if (n < 0) return fail(ASR_EINVAL, "n < 0");
+  if (n == 0) return ok();
+  if (!x || !r16 || !out) return fail(ASR_EINVAL, "NULL buffer");
+  if (!aligned(x, 4) || !aligned(r16, 2) || !aligned(out, 2))
+    return fail(ASR_EALIGN, "buffer not aligned to its element size");
+  const int64_t blocks = (n + asr::kBlock - 1) / asr::kBlock;
+  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(blocks, 1 << 16));
+  hipError_t e = launch(asr::sr_given_bits, grid, static_cast<hipStream_t>(stream_ptr), x, r16,
+                        out, n);
+  if (e != hipSuccess) return hip_fail(e, "sr launch");
+  return ok();
 }
 
 int asr_f32_sqrt_div(const float* a, const float* b, float* sqrt_out, float* div_out,

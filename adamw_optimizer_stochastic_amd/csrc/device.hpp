@@ -93,8 +93,29 @@ __device__ __forceinline__ bool f32_bits_is_nan(uint32_t u) {
 // Stochastic rounding: add the 16 random bits to the dropped half, keep the
 // high half. A NaN keeps its high half with the quiet bit forced on, so no
 // payload can carry into the exponent or the sign.
-__device__ __forceinline__ uint32_t round_sr(uint32_t u, uint32_t r16) {
+//
+// gfx950 has this conversion in hardware (v_cvt_sr_bf16_f32). It takes its
+// 16 random bits from the HIGH half of the 32-bit random operand and
+// otherwise computes exactly the rule above, NaN, Inf, subnormals and
+// overflow included; the test suite checks that against the reference
+// implementation for every f32 input at several random values and for every
+// random value at sampled inputs. ASR_HW_SR=0 selects the integer form.
+#ifndef ASR_HW_SR
+#define ASR_HW_SR 1
+#endif
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t round_sr_int(uint32_t u, uint32_t r16) {
   return f32_bits_is_nan(u) ? ((u >> 16) | 0x0040u) : ((u + r16) >> 16);
+}
+
+__device__ __forceinline__ uint32_t round_sr(uint32_t u, uint32_t r16) {
+  if constexpr (ASR_HW_SR) {
+    const bf16x2 v = __builtin_amdgcn_cvt_sr_bf16_f32(bf16x2{}, __uint_as_float(u), r16 << 16, false);
+    return __builtin_bit_cast(uint32_t, v) & 0xFFFFu;
+  } else {
+    return round_sr_int(u, r16);
+  }
 }
 
 // Round to nearest, ties to even; NaN as above.

@@ -140,3 +140,17 @@ def f32_sqrt_div(a, b):
         _abi.asr_f32_sqrt_div(a.data_ptr(), b.data_ptr(), s.data_ptr(), d.data_ptr(), a.numel(),
                               _stream(a.device))
     return s, d
+
+
+def sr_bf16_given_bits(x, r16, *, out=None):
+    """SR f32 -> bf16 with caller-supplied random bits r16 (int16 tensor whose
+    bit patterns are the 16-bit random values)."""
+    _require_gpu(x, "x")
+    _require_gpu(r16, "r16")
+    if x.dtype != torch.float32 or r16.dtype != torch.int16 or r16.numel() != x.numel():
+        raise ValueError("x must be float32 and r16 int16 of the same size")
+    out = _convert_args(x, out)
+    with torch.cuda.device(x.device):
+        _abi.asr_sr_bf16_given_bits(x.data_ptr(), r16.data_ptr(), out.data_ptr(), x.numel(),
+                                    _stream(x.device))
+    return out

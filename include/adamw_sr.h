@@ -178,6 +178,19 @@ int asr_cvt_f32_bf16_rn(const float* in, uint16_t* out, int64_t n,
                         void* stream);
 
 /*
+ * Stochastic rounding f32 -> bf16 with the random bits supplied by the
+ * caller: out[i] = SR(x[i], r16[i]) under the rule at the top of this file.
+ * ("Add stochastic rounding and philox RNG helpers", Primitives: the
+ * rounding primitive takes its random bits as an input.) The same device
+ * rounding as asr_adamw_step and asr_cvt_f32_bf16_sr, so it is the hook
+ * that checks the rounding apart from the generator.
+ * x: device, n f32; r16: device, n uint16 random values; out: device, n bf16
+ * patterns. Natural alignment. Errors: ASR_EINVAL, ASR_EALIGN, ASR_EHIP.
+ */
+int asr_sr_bf16_given_bits(const float* x, const uint16_t* r16, uint16_t* out,
+                           int64_t n, void* stream);
+
+/*
  * Test support: the binary32 square root and division exactly as the AdamW
  * kernel evaluates them: sqrt_out[i] = sqrt(a[i]), div_out[i] = a[i] / b[i],
  * both correctly rounded (to nearest even, subnormals kept).

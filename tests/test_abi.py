@@ -141,3 +141,14 @@ def test_other_entry_points_argument_errors():
     assert _status(_abi.asr_f32_sqrt_div, 0x1000, 0x2000, 0x3000, 0x4001, 3, None) == E.ASR_EALIGN
     assert _status(_abi.asr_f32_sqrt_div, 0, 0, 0, 0, -1, None) == E.ASR_EINVAL
     assert _status(_abi.asr_adamw_host_scalars, 1e-3, 0.9, 0.999, 1e-8, 0.01, 0) == E.ASR_EINVAL
+
+
+def test_sr_given_bits_argument_errors():
+    E = _abi
+    f = _abi.asr_sr_bf16_given_bits
+    assert _status(f, 0x1000, 0x2000, 0x3000, -1, None) == E.ASR_EINVAL
+    assert _status(f, 0, 0x2000, 0x3000, 4, None) == E.ASR_EINVAL
+    assert _status(f, 0x1002, 0x2000, 0x3000, 4, None) == E.ASR_EALIGN
+    assert _status(f, 0x1000, 0x2001, 0x3000, 4, None) == E.ASR_EALIGN
+    assert _status(f, 0x1000, 0x2000, 0x3001, 4, None) == E.ASR_EALIGN
+    assert _status(f, 0, 0, 0, 0, None) == E.ASR_OK
