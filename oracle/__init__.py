@@ -10,6 +10,9 @@ Sources (the pages are cited by title and section):
   * "Add stochastic rounding and philox RNG helpers" (FlyDSL pull request),
     Primitives and Tests sections: the add-and-truncate rounding rule and the
     counter-based Philox generator.
+  * The same FlyDSL page, GEMM and Tests sections: a bf16 GEMM whose f32
+    accumulator is rounded to bf16 by RN or by SR keyed per output element
+    (oracle/gemm.py).
   * "adamw-sr" (kernels hub page), intro, Usage, Method, Correctness sections:
     the decoupled-weight-decay AdamW step, fp32 states, bf16 write-back by
     stochastic rounding, random bits tied to the key (seed, step) and to
@@ -47,3 +50,7 @@ from .adamw import (  # noqa: F401
 )
 from .stream import philox_fill  # noqa: F401,E402
 from .convert import cvt_f32_bf16_sr, cvt_f32_bf16_rn  # noqa: F401,E402
+from .gemm import (  # noqa: F401,E402
+    gemm_exact, gemm_exact_scalar, gemm_dot, abs_products, f32_sum_bound,
+    gemm_round, gemm_round_at,
+)
