@@ -12,8 +12,8 @@ The library is loaded on first use; if it is missing, calls raise.
 from .optim import AdamWSR  # noqa: F401
 from . import ops  # noqa: F401
 from .ops import (  # noqa: F401
-    adamw_step, philox_4x32_fill, cvt_f32_bf16_sr, cvt_f32_bf16_rn, AsrError,
+    adamw_step, philox_4x32_fill, cvt_f32_bf16_sr, cvt_f32_bf16_rn, gemm_bf16, AsrError,
 )
 
 __all__ = ["AdamWSR", "ops", "adamw_step", "philox_4x32_fill", "cvt_f32_bf16_sr",
-           "cvt_f32_bf16_rn", "AsrError"]
+           "cvt_f32_bf16_rn", "gemm_bf16", "AsrError"]

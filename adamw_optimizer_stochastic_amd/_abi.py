@@ -16,7 +16,7 @@ from ._build import LIB_PATH
 ASR_OK, ASR_EINVAL, ASR_EDTYPE, ASR_EALIGN, ASR_EWORKSPACE, ASR_EHIP = range(6)
 ASR_F32, ASR_BF16 = 0, 1
 ASR_ROUND_SR, ASR_ROUND_RN = 0, 1
-ABI_VERSION = 100
+ABI_VERSION = 101
 
 STATUS_NAMES = {ASR_OK: "ASR_OK", ASR_EINVAL: "ASR_EINVAL", ASR_EDTYPE: "ASR_EDTYPE",
                 ASR_EALIGN: "ASR_EALIGN", ASR_EWORKSPACE: "ASR_EWORKSPACE",
@@ -58,6 +58,10 @@ _SIGNATURES = {
                                        _c.c_uint32, _c.c_uint64, _c.c_void_p]),
     "asr_cvt_f32_bf16_rn": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "asr_f32_sqrt_div": (_c.c_int, [_c.c_void_p] * 4 + [_c.c_int64, _c.c_void_p]),
+    "asr_gemm_bf16": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                 _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                                 _c.c_int32, _c.c_uint32, _c.c_uint32, _c.c_uint64,
+                                 _c.c_void_p]),
     "asr_sr_bf16_given_bits": (_c.c_int, [_c.c_void_p] * 3 + [_c.c_int64, _c.c_void_p]),
 }
 
@@ -147,6 +151,12 @@ def asr_cvt_f32_bf16_rn(inp, out, n, stream):
 
 def asr_f32_sqrt_div(a, b, sqrt_out, div_out, n, stream):
     _check(lib().asr_f32_sqrt_div(a, b, sqrt_out, div_out, n, stream), "asr_f32_sqrt_div")
+
+
+def asr_gemm_bf16(a, lda, b, ldb, c, ldc, c_f32, m, n, k, rounding, seed, step, base_index,
+                  stream):
+    _check(lib().asr_gemm_bf16(a, lda, b, ldb, c, ldc, c_f32, m, n, k, rounding, seed, step,
+                               base_index, stream), "asr_gemm_bf16")
 
 
 def asr_sr_bf16_given_bits(x, r16, out, n, stream):

@@ -1,7 +1,8 @@
 """Build step: compiles the HIP sources into the in-tree shared library.
 
-One translation unit (csrc/adamw_sr.hip, which includes csrc/device.hpp and
-include/adamw_sr.h) -> libadamw_sr.so, for gfx950 only. Flags that matter
+Two translation units (csrc/adamw_sr.hip: the AdamW step, the generator and
+the conversions; csrc/gemm_sr.hip: the GEMM; both include csrc/device.hpp,
+csrc/status.hpp and include/adamw_sr.h) -> libadamw_sr.so, for gfx950 only. Flags that matter
 for the arithmetic:
   -ffp-contract=off                          no fused multiply-adds (the
                                              sources also say so by pragma)
@@ -20,8 +21,10 @@ import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SOURCES = [os.path.join(PKG_DIR, "csrc", "adamw_sr.hip")]
+SOURCES = [os.path.join(PKG_DIR, "csrc", "adamw_sr.hip"),
+           os.path.join(PKG_DIR, "csrc", "gemm_sr.hip")]
 DEPENDS = SOURCES + [os.path.join(PKG_DIR, "csrc", "device.hpp"),
+                     os.path.join(PKG_DIR, "csrc", "status.hpp"),
                      os.path.join(ROOT, "include", "adamw_sr.h")]
 LIB_NAME = "libadamw_sr.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)

@@ -21,6 +21,7 @@
 // launch cover thousands of tensors: every workgroup takes whole chunks of
 // one tensor and finds its tensor by a wave-uniform binary search.
 #include "device.hpp"
+#include "status.hpp"
 
 #include <adamw_sr.h>
 
@@ -374,7 +375,7 @@ sqrt_div(const float* __restrict__ a, const float* __restrict__ b,
 }  // namespace asr
 
 // =========================================================== host side
-namespace {
+namespace asr_host {
 
 thread_local std::string g_last_error;
 
@@ -387,6 +388,19 @@ int ok() {
   g_last_error.clear();
   return ASR_OK;
 }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ASR_EHIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                            hipGetErrorString(e) + ")");
+}
+
+}  // namespace asr_host
+
+namespace {
+
+using asr_host::fail;
+using asr_host::hip_fail;
+using asr_host::ok;
 
 // Launches `kernel` with one block size for all kernels of the library;
 // the arguments are converted to the kernel's parameter types first.
@@ -408,11 +422,6 @@ template <typename... KArgs, typename... Args>
 hipError_t launch(void (*kernel)(KArgs...), uint32_t grid, hipStream_t stream,
                   Args&&... args) {
   return launch_lds(kernel, grid, 0, stream, std::forward<Args>(args)...);
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return fail(ASR_EHIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
-                            hipGetErrorString(e) + ")");
 }
 
 bool aligned(const void* p, uintptr_t a) {
@@ -621,7 +630,7 @@ extern "C" {
 
 int asr_abi_version(void) { return ASR_ABI_VERSION; }
 
-const char* asr_last_error(void) { return g_last_error.c_str(); }
+const char* asr_last_error(void) { return asr_host::g_last_error.c_str(); }
 
 size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors) {
   if (n_tensors <= 0 || !tensors) return 0;

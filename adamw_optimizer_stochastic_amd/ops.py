@@ -126,6 +126,52 @@ def cvt_f32_bf16_rn(x, *, out=None):
     return out
 
 
+def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, out_f32=None):
+    """C = A B^T for bf16 A (M x K) and B (N x K), rounded to bf16.
+
+    rounding "rn" (round to nearest even) or "sr" (stochastic: element
+    (m, n) uses stream position base_index + m*N + n under key (seed,
+    step)). ``out``: optional bf16 (M x N) destination, row stride >= N;
+    ``out_f32``: optional float32 (M x N) tensor with the same strides as
+    ``out`` that also receives the unrounded result. Returns ``out``.
+    """
+    for t, name in ((a, "a"), (b, "b")):
+        _require_gpu(t, name)
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D bfloat16 tensor")
+        if t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit stride along K")
+    if a.device != b.device:
+        raise ValueError("a and b must be on the same device")
+    if a.shape[1] != b.shape[1]:
+        raise ValueError(f"K mismatch: a is {tuple(a.shape)}, b is {tuple(b.shape)}")
+    if rounding not in ("rn", "sr"):
+        raise ValueError("rounding must be 'rn' or 'sr'")
+    m, k = a.shape
+    n = b.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (m, n) or out.device != a.device \
+            or (m > 0 and n > 0 and out.stride(1) != 1):
+        raise ValueError("out must be a bfloat16 (M, N) tensor with unit column stride")
+    ldc = out.stride(0) if m > 1 else max(n, 1)
+    f32_ptr = None
+    if out_f32 is not None:
+        if out_f32.dtype != torch.float32 or tuple(out_f32.shape) != (m, n) \
+                or out_f32.device != a.device or out_f32.stride() != out.stride():
+            raise ValueError("out_f32 must be a float32 (M, N) tensor with out's strides")
+        f32_ptr = out_f32.data_ptr()
+    # a row stride only matters when there is a second row and a K to walk
+    lda = a.stride(0) if m > 1 and k > 0 else max(k, 8)
+    ldb = b.stride(0) if n > 1 and k > 0 else max(k, 8)
+    code = ASR_ROUND_SR if rounding == "sr" else ASR_ROUND_RN
+    with torch.cuda.device(a.device):
+        _abi.asr_gemm_bf16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, f32_ptr,
+                           m, n, k, code, int(seed), int(step), int(base_index) % (1 << 64),
+                           _stream(a.device))
+    return out
+
+
 def f32_sqrt_div(a, b):
     """(sqrt(a), a / b) as the AdamW kernel evaluates them (test support)."""
     for t, name in ((a, "a"), (b, "b")):

@@ -18,6 +18,11 @@ Workloads (sizes as used by the tests and the benchmark):
   * llama3_8b: the parameter list of a Llama-3-8B-shaped model (291
              tensors, 8,030,261,248 elements), bf16 matrices ~N(0, 0.02),
              RMSNorm weights 1.0, bf16 grads ~N(0, 1e-3), f32 m = v = 0.
+  * gemm:    bf16 operands of C = A B^T. "randn": A ~N(0, 1) (activations),
+             B ~N(0, 0.02) (weights); "int": integers uniform in [-8, 8]
+             (every f32 partial sum is then exact). The full-size case is
+             the gate/up projection of one Llama-3-8B MLP over 8,192
+             tokens: M = 8192, N = 14336, K = 4096.
 """
 
 import numpy as np
@@ -53,6 +58,9 @@ def numel(shape):
 
 # ------------------------------------------------------------ host draws
 CFG_SMALL, CFG_SUBULP, CFG_F32, CFG_CONVERT, CFG_SHARDS, CFG_LLAMA = 1, 2, 3, 4, 5, 6
+CFG_GEMM = 7
+
+GEMM_LLAMA3_8B_MLP_UP = dict(m=8192, n=LLAMA3_8B["ffn"], k=LLAMA3_8B["hidden"])
 
 
 def host_rng(cfg_id, seed=0, step=0):
@@ -124,3 +132,26 @@ def llama3_8b_state(device, seed=0, param_std=0.02, grad_std=1e-3, cfg=LLAMA3_8B
                         base_index=base))
         base += n
     return out
+
+
+def gemm_operands_host(m, n, k, kind, seed=0):
+    """bf16 patterns of A (m x k) and B (n x k)."""
+    rng = host_rng(CFG_GEMM, seed, (m * 1000003 + n) * 1000003 + k)
+    if kind == "int":
+        a = rng.integers(-8, 9, size=(m, k)).astype(np.float32)
+        b = rng.integers(-8, 9, size=(n, k)).astype(np.float32)
+    elif kind == "randn":
+        a = rng.standard_normal((m, k)).astype(np.float32)
+        b = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    return f32_to_bf16_bits(a).reshape(m, k), f32_to_bf16_bits(b).reshape(n, k)
+
+
+def gemm_operands_device(m, n, k, device, seed=0):
+    """The "randn" operands drawn on the device (for sizes too large to draw
+    on the host): bf16 tensors A (m x k) and B (n x k)."""
+    gen = device_generator(device, CFG_GEMM, seed)
+    a = device_normal(m * k, 1.0, gen, device, torch.bfloat16).view(m, k)
+    b = device_normal(n * k, 0.02, gen, device, torch.bfloat16).view(n, k)
+    return a, b

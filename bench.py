@@ -8,8 +8,14 @@ in HBM), the dominant kernel's achieved HBM bandwidth against the 8 TB/s
 peak (algorithmic bytes: 22 per element), and the CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|shards|convert]
+    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|shards|convert|gemm]
     python bench.py --copy-probe      # plain copy of known size (counter scaling)
+
+The gemm workload times the bf16 GEMM with the SR epilogue on the gate/up
+projection of one Llama-3-8B MLP over 8,192 tokens (M=8192, N=14336,
+K=4096; --gemm-shape M,N,K overrides), against the 2.5 PFLOP/s dense bf16
+matrix-core peak, with the same GEMM under RN and torch.matmul (the vendor
+library, RN) timed beside it for context.
 """
 
 import argparse
@@ -188,6 +194,92 @@ def run_convert(args, torch, ops, wl):
                          "kernel_ms_avg": kernel_ms}}
 
 
+GEMM_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def _time_launches(torch, stream, fn, steps):
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        events[k][0].record(stream)
+        fn()
+        events[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps, sum(a.elapsed_time(b) for a, b in events) / steps
+
+
+def gemm_cpu_baseline(m, n, k, rows=256):
+    """The oracle's GEMM (binary64 product, then SR of the f32 result) on
+    `rows` rows of the same shape, timed on the host."""
+    import numpy as np
+    import oracle
+    from adamw_optimizer_stochastic_amd import workloads as wl
+    a, b = wl.gemm_operands_host(rows, n, k, "randn", seed=0)
+    t0 = time.perf_counter()
+    c = oracle.gemm_exact(a, b).astype(np.float32)
+    oracle.gemm_round(c, "sr", 7, 1, 0)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": 2.0 * rows * n * k / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} of the {m} rows (numpy binary64 matmul, then the SR "
+                      f"rounding), {dt:.1f} s"}
+
+
+def run_gemm(args, torch, ops, wl):
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.gemm_shape:
+        m, n, k = (int(x) for x in args.gemm_shape.split(","))
+        name = f"gemm_{m}x{n}x{k}"
+    else:
+        m, n, k = (wl.GEMM_LLAMA3_8B_MLP_UP[x] for x in ("m", "n", "k"))
+        name = "llama3_8b_mlp_up_proj_8192_tokens"
+    a, b = wl.gemm_operands_device(m, n, k, dev, seed=0)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = 2.0 * m * n * k
+    step = [0]
+
+    def sr():
+        step[0] += 1
+        ops.gemm_bf16(a, b, rounding="sr", seed=7, step=step[0], out=c)
+
+    def rn():
+        ops.gemm_bf16(a, b, rounding="rn", out=c)
+
+    def lib():
+        torch.matmul(a, b.t(), out=c)
+
+    for fn in (sr, rn, lib):
+        for _ in range(args.warmup):
+            fn()
+    wall, kernel_ms = _time_launches(torch, stream, sr, args.steps)
+    _, rn_ms = _time_launches(torch, stream, rn, args.steps)
+    _, lib_ms = _time_launches(torch, stream, lib, args.steps)
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    return {
+        "metric": "bf16 GEMM with stochastic-rounding epilogue, TFLOP/s, 1 GPU",
+        "value": flops / wall / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "m": m, "n": n, "k": k, "layout": "C = A B^T",
+                   "rounding": "sr", "accumulate": "f32"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": GEMM_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / GEMM_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "asr_gemm::gemm_bf16<256x256 tile, SR>",
+                     "kernel_ms_avg": kernel_ms},
+        "context": {"same_kernel_rn_ms": rn_ms,
+                    "same_kernel_rn_tflops": flops / (rn_ms * 1e-3) / 1e12,
+                    "torch_matmul_rn_ms": lib_ms,
+                    "torch_matmul_rn_tflops": flops / (lib_ms * 1e-3) / 1e12,
+                    "sr_over_rn": kernel_ms / rn_ms},
+    }
+
+
 def run_copy_probe(args, torch):
     """A plain device copy of 8 GiB (torch's copy kernel), for scaling the
     FETCH_SIZE/WRITE_SIZE counters: it moves exactly 8 GiB each way."""
@@ -212,7 +304,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "shards", "convert"])
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "shards", "convert", "gemm"])
+    ap.add_argument("--gemm-shape", default=None, help="M,N,K for --workload gemm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -228,6 +321,10 @@ def main():
     if not args.no_cpu_baseline and not args.copy_probe and args.workload == "llama3_8b":
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline()
+    if not args.no_cpu_baseline and not args.copy_probe and args.workload == "gemm":
+        print("[bench] cpu baseline (oracle gemm) ...", file=sys.stderr, flush=True)
+        cpu = gemm_cpu_baseline(8192, 14336, 4096) if not args.gemm_shape else \
+            gemm_cpu_baseline(*(int(x) for x in args.gemm_shape.split(",")))
 
     import torch
     from adamw_optimizer_stochastic_amd import ops
@@ -242,6 +339,8 @@ def main():
           file=sys.stderr, flush=True)
     if args.workload == "convert":
         res = run_convert(args, torch, ops, wl)
+    elif args.workload == "gemm":
+        res = run_gemm(args, torch, ops, wl)
     else:
         res = run_adamw(args, torch, ops, wl)
     if cpu is not None:

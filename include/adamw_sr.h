@@ -191,6 +191,44 @@ int asr_sr_bf16_given_bits(const float* x, const uint16_t* r16, uint16_t* out,
                            int64_t n, void* stream);
 
 /*
+ * bf16 GEMM with a stochastic-rounding (or round-to-nearest) epilogue.
+ * ("Add stochastic rounding and philox RNG helpers", GEMM section: the f32
+ * accumulator of a bf16 GEMM is converted to bf16 by SR keyed per output
+ * element from a seed, RN being the other rounding; Tests: SR within
+ * tolerance of RN, seed-dependent, reproducible.)
+ *
+ *   C[m][n] = round( sum_k A[m][k] * B[n][k] )     0 <= m < M, 0 <= n < N
+ *
+ * i.e. C = A * B^T with A (M x K) and B (N x K) both row-major, K
+ * contiguous (the layout of x and W in a linear layer y = x W^T). The sum
+ * is accumulated in f32 on the matrix cores in an order of the library's
+ * choosing (fixed for given M, N, K, so results are reproducible).
+ * rounding ASR_ROUND_SR: element (m, n) is rounded with the 16 random bits
+ * of stream position base_index + m*N + n under key (seed, step) -- the
+ * stream and rule of asr_cvt_f32_bf16_sr, so C equals that conversion of
+ * the f32 result bit for bit, and a block of rows [r0, r1) computed alone
+ * with base_index + r0*N reproduces those rows of the whole product.
+ * rounding ASR_ROUND_RN: round to nearest even (seed, step, base_index
+ * unused).
+ *
+ * a: device bf16 patterns, row m at a + m*lda; b: device, row n at
+ * b + n*ldb; c: device bf16 patterns, row m at c + m*ldc; c_f32: NULL, or
+ * a device f32 buffer with the same row stride ldc that receives the
+ * unrounded f32 result. No output may overlap an input.
+ * Requirements: 0 <= M, N, K < 2**31; K, lda, ldb multiples of 8; lda >= K,
+ * ldb >= K, ldc >= N; a and b 16-byte aligned; c and c_f32 aligned to
+ * their element size; base_index + M*N <= 2**64. M or N = 0 writes
+ * nothing; K = 0 writes zeros.
+ * Errors: ASR_EINVAL (sizes, strides, rounding, NULL), ASR_EALIGN,
+ * ASR_EHIP (launch failure). Runs on `stream`; does not synchronize.
+ */
+int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b,
+                  int64_t ldb, uint16_t* c, int64_t ldc, float* c_f32,
+                  int64_t m, int64_t n, int64_t k, int32_t rounding,
+                  uint32_t seed, uint32_t step, uint64_t base_index,
+                  void* stream);
+
+/*
  * Test support: the binary32 square root and division exactly as the AdamW
  * kernel evaluates them: sqrt_out[i] = sqrt(a[i]), div_out[i] = a[i] / b[i],
  * both correctly rounded (to nearest even, subnormals kept).
@@ -207,7 +245,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 100
+#define ASR_ABI_VERSION 101
 
 #ifdef __cplusplus
 }

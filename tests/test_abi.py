@@ -152,3 +152,32 @@ def test_sr_given_bits_argument_errors():
     assert _status(f, 0x1000, 0x2001, 0x3000, 4, None) == E.ASR_EALIGN
     assert _status(f, 0x1000, 0x2000, 0x3001, 4, None) == E.ASR_EALIGN
     assert _status(f, 0, 0, 0, 0, None) == E.ASR_OK
+
+
+def test_gemm_argument_errors():
+    """Every check of asr_gemm_bf16 returns before the first HIP call."""
+    E = _abi
+    f = _abi.asr_gemm_bf16
+
+    def g(a=0x1000, lda=64, b=0x2000, ldb=64, c=0x3000, ldc=32, c32=None, m=16, n=32, k=64,
+          rounding=E.ASR_ROUND_SR, base=0):
+        return _status(f, a, lda, b, ldb, c, ldc, c32, m, n, k, rounding, 1, 2, base, None)
+
+    assert g(m=-1) == E.ASR_EINVAL
+    assert g(k=2**31) == E.ASR_EINVAL
+    assert g(rounding=2) == E.ASR_EINVAL
+    assert g(a=0) == E.ASR_EINVAL
+    assert g(c=0) == E.ASR_EINVAL
+    assert g(lda=56) == E.ASR_EINVAL          # lda < k
+    assert g(ldc=31) == E.ASR_EINVAL          # ldc < n
+    assert g(k=60, lda=64, ldb=64) == E.ASR_EALIGN   # k not a multiple of 8
+    assert g(lda=68) == E.ASR_EALIGN
+    assert g(a=0x1008) == E.ASR_EALIGN        # A not 16-byte aligned
+    assert g(c=0x3001) == E.ASR_EALIGN
+    assert g(c32=0x4002) == E.ASR_EALIGN
+    assert g(base=2**64 - 16 * 32 + 1) == E.ASR_EINVAL   # positions past 2**64
+    assert "2**64" in _abi.asr_last_error()
+    # nothing to compute: no error, nothing touched
+    assert g(m=0, a=0, b=0, c=0) == E.ASR_OK
+    assert g(n=0, a=0, b=0, c=0) == E.ASR_OK
+    assert _abi.asr_last_error() == ""

@@ -1,0 +1,212 @@
+"""The bf16 GEMM with an SR/RN epilogue (asr_gemm_bf16) against the oracle.
+
+* Integer operands in [-8, 8]: every f32 partial sum is exact whatever the
+  summation order, so the kernel's f32 result must equal the exact product
+  and both roundings must equal the oracle's roundings of it, bit for bit.
+* N(0, 1) x N(0, 0.02) operands: the f32 result lies within the bound any
+  f32 summation order meets, and the bf16 output equals the oracle's
+  rounding (RN, or SR at positions base + m*N + n) of the kernel's own f32
+  result, bit for bit.
+* The FlyDSL page's GEMM acceptance (Tests section): SR within tolerance of
+  RN, changes with the seed, reproducible for a fixed seed; plus
+  unbiasedness over seeds, a block of rows computed alone, strided and
+  unaligned outputs, and the degenerate sizes.
+
+Shapes span several tiles of both tile configurations (128 x 128 and
+256 x 256 workgroup tiles; the larger is used once there are at least 256
+of them) with ragged edges in M, N and K.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adamw_optimizer_stochastic_amd import ops, workloads as wl
+from _gpu_util import gpu, require_gpu, announce, to_host, assert_bits_equal, bf16_tensor
+
+pytestmark = gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _run(a_bits, b_bits, rounding, seed=0, step=0, base=0, f32=True):
+    a = bf16_tensor(a_bits)
+    b = bf16_tensor(b_bits)
+    m, n = a.shape[0], b.shape[0]
+    c32 = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda") if f32 else None
+    c = ops.gemm_bf16(a, b, rounding=rounding, seed=seed, step=step, base_index=base,
+                      out_f32=c32)
+    torch.cuda.synchronize()
+    return to_host(c), (to_host(c32) if f32 else None)
+
+
+# (M, N, K): single elements, one partial tile, several 128-tiles with
+# ragged edges, K not a multiple of 64, and the 256-tile path (>= 256 tiles)
+# with ragged M and N.
+SHAPES = [(1, 1, 8), (5, 3, 16), (33, 65, 72), (128, 128, 64), (130, 257, 200),
+          (256, 512, 1024), (4100, 4097, 136)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_integer_operands_exact(shape):
+    m, n, k = shape
+    announce("gemm int exact", shape)
+    a, b = wl.gemm_operands_host(m, n, k, "int", seed=1)
+    exact = oracle.gemm_exact(a, b)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    seed, step, base = 1234, 7, 40
+    c_sr, c32 = _run(a, b, "sr", seed, step, base)
+    assert_bits_equal(c32.reshape(-1), exact.astype(np.float32).reshape(-1), "f32 result")
+    want_sr = oracle.gemm_round(exact.astype(np.float32), "sr", seed, step, base)
+    assert_bits_equal(c_sr.reshape(-1), want_sr.reshape(-1), "SR output")
+    c_rn, c32_rn = _run(a, b, "rn")
+    assert_bits_equal(c32_rn.reshape(-1), c32.reshape(-1), "f32 result of the RN run")
+    want_rn = oracle.gemm_round(exact.astype(np.float32), "rn")
+    assert_bits_equal(c_rn.reshape(-1), want_rn.reshape(-1), "RN output")
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 512), (64, 96, 4096), (4096, 4096, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_normal_operands_bound_and_rounding(shape):
+    m, n, k = shape
+    announce("gemm randn", shape)
+    a, b = wl.gemm_operands_host(m, n, k, "randn", seed=2)
+    seed, step, base = 99, 3, 0
+    c_sr, c32 = _run(a, b, "sr", seed, step, base)
+    err = np.abs(c32.astype(np.float64) - oracle.gemm_exact(a, b))
+    bound = oracle.f32_sum_bound(a, b)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300))}"
+    want = oracle.gemm_round(c32, "sr", seed, step, base)
+    assert_bits_equal(c_sr.reshape(-1), want.reshape(-1), "SR output")
+    c_rn, c32_rn = _run(a, b, "rn")
+    assert_bits_equal(c32_rn.reshape(-1), c32.reshape(-1), "f32 result of the RN run")
+    assert_bits_equal(c_rn.reshape(-1), oracle.gemm_round(c32, "rn").reshape(-1), "RN output")
+
+
+def _bf16_steps_apart(x, y):
+    """Distance in bf16 steps between two arrays of finite bf16 patterns
+    (patterns mapped to a monotone integer line)."""
+    def line(h):
+        h = h.astype(np.int64)
+        return np.where(h & 0x8000, -(h & 0x7FFF), h)
+    return np.abs(line(x) - line(y))
+
+
+def test_acceptance_tolerance_seed_reproducible():
+    announce("gemm acceptance")
+    m, n, k = 512, 384, 1024
+    a, b = wl.gemm_operands_host(m, n, k, "randn", seed=3)
+    rn, c32 = _run(a, b, "rn")
+    sr1, _ = _run(a, b, "sr", seed=1, step=1)
+    sr1b, _ = _run(a, b, "sr", seed=1, step=1)
+    sr2, _ = _run(a, b, "sr", seed=2, step=1)
+    sr3, _ = _run(a, b, "sr", seed=1, step=2)
+    # within one bf16 step of RN (SR picks one of the two neighbours of the
+    # f32 result, RN the nearer one)
+    assert _bf16_steps_apart(sr1, rn).max() <= 1
+    # reproducible for a fixed key
+    assert np.array_equal(sr1, sr1b)
+    # changes with the seed, and with the step: an element that rounds up
+    # with probability p differs between two keys with probability
+    # 2p(1 - p), a third on average over the inexact elements
+    inexact = (oracle.f32_bits(c32) & 0xFFFF) != 0
+    for other in (sr2, sr3):
+        frac = np.mean(other[inexact] != sr1[inexact])
+        assert 0.2 < frac < 0.8, frac
+
+
+def test_unbiased_over_seeds():
+    announce("gemm unbiased")
+    m, n, k = 256, 256, 512
+    a, b = wl.gemm_operands_host(m, n, k, "randn", seed=4)
+    _, c32 = _run(a, b, "rn")
+    x = c32.astype(np.float64)
+    u = oracle.f32_bits(c32)
+    lo = oracle.bf16_to_f32(u >> 16).astype(np.float64)          # toward zero
+    hi = oracle.bf16_to_f32((u >> 16) + 1).astype(np.float64)    # away from zero
+    p = np.abs(x - lo) / np.abs(hi - lo)   # probability of rounding away from zero
+    seeds = 64
+    ups = np.zeros(x.shape, dtype=np.int64)
+    for s in range(seeds):
+        sr, _ = _run(a, b, "sr", seed=1000 + s, step=5, f32=False)
+        v = oracle.bf16_to_f32(sr).astype(np.float64)
+        assert np.all((v == lo) | (v == hi))
+        ups += v == hi
+    # the mean of the SR values is the f32 result: averaged over all
+    # elements, the error in ulps has standard deviation 0.5 / sqrt(64 m n)
+    err_ulps = ups / seeds - p
+    assert abs(err_ulps.mean()) < 6 * 0.5 / np.sqrt(seeds * x.size)
+    # and each element's count of round-ups is Binomial(64, p): the mean
+    # squared z-score is 1 (elements with p away from 0 and 1, where the
+    # normal approximation holds)
+    mid = (p > 1 / 16) & (p < 15 / 16)
+    z2 = (ups[mid] - seeds * p[mid]) ** 2 / (seeds * p[mid] * (1 - p[mid]))
+    assert mid.sum() > x.size // 2
+    assert 0.93 < z2.mean() < 1.07, z2.mean()
+
+
+def test_row_block_alone_reproduces_rows():
+    announce("gemm row block")
+    m, n, k = 700, 300, 264
+    a, b = wl.gemm_operands_host(m, n, k, "randn", seed=5)
+    seed, step, base = 17, 9, 1 << 40
+    whole, _ = _run(a, b, "sr", seed, step, base, f32=False)
+    r0, r1 = 129, 517
+    part, _ = _run(a[r0:r1], b, "sr", seed, step, base + r0 * n, f32=False)
+    assert np.array_equal(part, whole[r0:r1])
+
+
+def test_strided_unaligned_outputs():
+    announce("gemm strided/unaligned")
+    m, n, k = 97, 203, 48   # N odd: no 4-element groups, positions unaligned
+    a_bits, b_bits = wl.gemm_operands_host(m, n, k, "randn", seed=6)
+    a, b = bf16_tensor(a_bits), bf16_tensor(b_bits)
+    ldc = n + 6   # odd: element-wise stores
+    canary = -7.0
+    store = torch.full((m, ldc), canary, dtype=torch.bfloat16, device="cuda")
+    store32 = torch.full((m, ldc), canary, dtype=torch.float32, device="cuda")
+    c, c32 = store[:, :n], store32[:, :n]
+    seed, step, base = 5, 6, 3   # base not a multiple of 4
+    ops.gemm_bf16(a, b, rounding="sr", seed=seed, step=step, base_index=base, out=c, out_f32=c32)
+    torch.cuda.synchronize()
+    h = to_host(store)
+    h32 = to_host(store32)
+    assert np.all(h[:, n:] == to_host(torch.tensor([canary], dtype=torch.bfloat16))[0])
+    assert np.all(h32[:, n:] == np.float32(canary))
+    got32 = h32[:, :n]
+    err = np.abs(got32.astype(np.float64) - oracle.gemm_exact(a_bits, b_bits))
+    assert np.all(err <= oracle.f32_sum_bound(a_bits, b_bits))
+    want = oracle.gemm_round(got32, "sr", seed, step, base)
+    assert_bits_equal(np.ascontiguousarray(h[:, :n]).reshape(-1), want.reshape(-1), "strided SR")
+
+
+def test_f32_copy_does_not_change_the_result():
+    announce("gemm with/without f32 copy")
+    m, n, k = 1024, 1024, 2048
+    a, b = wl.gemm_operands_host(m, n, k, "randn", seed=7)
+    with32, _ = _run(a, b, "sr", 3, 4, 8)
+    without, _ = _run(a, b, "sr", 3, 4, 8, f32=False)
+    assert np.array_equal(with32, without)
+
+
+def test_degenerate_sizes():
+    announce("gemm degenerate")
+    dev = "cuda"
+    a = torch.zeros((0, 16), dtype=torch.bfloat16, device=dev)
+    b = torch.ones((4, 16), dtype=torch.bfloat16, device=dev)
+    assert ops.gemm_bf16(a, b).shape == (0, 4)
+    # K = 0: the empty sum, +0 under both roundings
+    a0 = torch.empty((5, 0), dtype=torch.bfloat16, device=dev)
+    b0 = torch.empty((7, 0), dtype=torch.bfloat16, device=dev)
+    for r in ("rn", "sr"):
+        out = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device=dev)
+        ops.gemm_bf16(a0, b0, rounding=r, seed=1, step=1, out=out)
+        torch.cuda.synchronize()
+        assert np.all(to_host(out) == 0)
+    with pytest.raises(ops.AsrError):
+        ops.gemm_bf16(torch.ones((4, 12), dtype=torch.bfloat16, device=dev),
+                      torch.ones((4, 12), dtype=torch.bfloat16, device=dev))  # K % 8 != 0
