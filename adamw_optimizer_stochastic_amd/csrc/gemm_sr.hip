@@ -52,37 +52,55 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-constexpr int kBK = 64;            // K elements per LDS stage
-constexpr int kRowBytes = kBK * 2;  // 128 bytes: 8 chunks of 16 bytes
-constexpr int kSlabRows = 8;       // rows one wave-wide 16-byte DMA fills
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;         // tile rows per group in the tile order
-
-// Byte offset of 16-byte chunk c of tile row r within a stage region. The
-// XOR spreads the rows a ds_read_b128 touches over all banks: rows r and
-// r+1 share a 256-byte bank period, and (r >> 1) & 7 takes eight values over
-// 16 consecutive rows.
-__device__ __forceinline__ uint32_t chunk_offset(uint32_t r, uint32_t c) {
-  return r * kRowBytes + ((c ^ ((r >> 1) & 7u)) << 4);
-}
+constexpr int kDmaBytes = 1024;    // LDS bytes one wave-wide 16-byte-per-lane DMA fills
+#ifndef ASR_GEMM_PREFETCH
+#define ASR_GEMM_PREFETCH 1
+#endif
+constexpr bool kPrefetch = ASR_GEMM_PREFETCH;  // read fragments one MFMA step ahead
+#ifndef ASR_GEMM_SCHEDULE
+#define ASR_GEMM_SCHEDULE 1
+#endif
+constexpr bool kSchedule = ASR_GEMM_SCHEDULE && ASR_GEMM_PREFETCH;  // see schedule_step
 
 // Source of chunks outside the matrices (rows past M or N, columns past K).
 __device__ __align__(16) uint4 g_zero_chunk;
 
-template <int BM_, int BN_, int WM_, int WN_>
+// Workgroup tile BM x BN, wave tile WM x WN, K in stages of BK (32 or 64),
+// STAGES stages in LDS.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
   static constexpr int kWaves = kWavesM * kWavesN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kFragM = WM / 32, kFragN = WN / 32;
+  static constexpr int kRowBytes = BK * 2;                 // one row of a stage
+  static constexpr int kChunks = BK / 8;                   // 16-byte chunks per row
+  static constexpr int kSlabRows = kDmaBytes / kRowBytes;  // rows per wave-wide DMA
   static constexpr int kSlabs = (BM + BN) / kSlabRows;
-  static constexpr int kSlabsPerWave = kSlabs / kWaves;
+  static constexpr int kSlabsPerWave = kSlabs / kWaves;    // DMAs per lane per stage
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static constexpr int kLdsBytes = STAGES * kStageBytes;
+  static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
   static_assert(kSlabs % kWaves == 0, "every wave fills the same number of slabs");
   static_assert(BM % kSlabRows == 0, "a slab lies in A or in B");
+  static_assert(STAGES >= 2 && kLdsBytes <= 160 * 1024, "LDS budget");
+
+  // Position of 16-byte chunk c in tile row r. A ds_read_b128 is served 16
+  // lanes at a time over 64 four-byte banks (256 bytes); its 16 lanes read
+  // one chunk index from 16 consecutive rows, and the XOR gives those rows
+  // 16 distinct bank ranges: 128-byte rows pair up in a 256-byte period and
+  // (r >> 1) & 7 separates the 8 pairs; 64-byte rows come four to a period
+  // and (r >> 2) & 3 separates the 4 periods.
+  __device__ static __forceinline__ uint32_t chunk_pos(uint32_t r, uint32_t c) {
+    return BK == 64 ? (c ^ ((r >> 1) & 7u)) : (c ^ ((r >> 2) & 3u));
+  }
+  __device__ static __forceinline__ uint32_t chunk_offset(uint32_t r, uint32_t c) {
+    return r * kRowBytes + (chunk_pos(r, c) << 4);
+  }
 };
 
 struct GemmArgs {
@@ -146,12 +164,61 @@ __device__ __forceinline__ void bits4(uint64_t p, bool pos4, uint32_t seed, uint
   }
 }
 
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ int32_t row_clamp(int32_t row, int32_t last) {
+  return row < last ? row : last;
+}
+
+// Workgroup barrier for the LDS ring: this wave's LDS reads are complete
+// (lgkmcnt(0)) and every wave has arrived. Unlike __syncthreads() it does
+// not wait for this wave's outstanding global->LDS copies (a release fence
+// would), which is the point of the ring; the caller waits for exactly the
+// copies it needs with wait_vmcnt. The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int N, typename F, int I = 0>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(std::integral_constant<int, I>{});
     static_for<N, F, I + 1>(static_cast<F&&>(f));
   }
+}
+
+// Instruction order of one MFMA step, imposed on the compiler's scheduler
+// (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x020 global
+// read, which includes the LDS-direct copies). The reads of the next step's
+// fragments and this step's copies are threaded between this step's MFMAs,
+// so they are issued early, into registers distinct from the ones the
+// MFMAs read, and the wait for them falls after a run of MFMAs.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
+template <typename Cfg, int KK, int STEPS, int DMAS>
+__device__ __forceinline__ void schedule_step() {
+  constexpr int kMfma = Cfg::kFragM * Cfg::kFragN;
+  constexpr int kReads = KK + 1 < STEPS ? Cfg::kFragM + Cfg::kFragN : 0;
+  static_for<kMfma>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (i < kReads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if constexpr (i >= kReads && i - kReads < DMAS)
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+  });
+  if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads - kMfma, 0);
+  if constexpr (kReads + DMAS > kMfma)
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead,
+                                         kReads + DMAS - kMfma > DMAS ? DMAS : kReads + DMAS - kMfma, 0);
 }
 
 // Writes output elements (m, n .. n+3) that lie inside C: the f32 values
@@ -193,42 +260,64 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   __shared__ __align__(1024) unsigned char smem[Cfg::kLdsBytes];
 
   const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = threadIdx.x >> 6;
+  // The wave index as a scalar: every LDS destination and global base below
+  // is then uniform and lives in scalar registers.
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t tm, tn;
   tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * BM;
   const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
-  // ---- this lane's share of the global -> LDS copies: one 16-byte chunk
-  // of row R = slab*8 + lane/8, at position lane%8 of that row.
-  const uint16_t* src[Cfg::kSlabsPerWave];
-  uint32_t kchunk[Cfg::kSlabsPerWave];  // element offset of the chunk in the stage
+  // ---- this lane's share of the global -> LDS copies. Slab j of this wave
+  // is rows slab * kSlabRows .. + kSlabRows - 1 of the stage (slab = wave +
+  // j * kWaves; the first kSlabsA slabs of every wave lie in A, the rest in
+  // B); the lane copies the 16-byte chunk at position lane % kChunks of row
+  // lane / kChunks. Its source is a scalar base (tile origin + K offset)
+  // plus a 32-bit per-lane byte offset. Rows past the edge of A or B are
+  // clamped to the last row: they only feed outputs that are not stored.
+  constexpr int kChunks = Cfg::kChunks;
+  constexpr int kSlabsA = BM / Cfg::kSlabRows / Cfg::kWaves;
+  static_assert((BM / Cfg::kSlabRows) % Cfg::kWaves == 0, "A slabs split evenly over waves");
+  const int32_t last_a = args.m - 1 - static_cast<int32_t>(m0);
+  const int32_t last_b = args.n - 1 - static_cast<int32_t>(n0);
+  uint32_t voff[Cfg::kSlabsPerWave];
 #pragma unroll
   for (int j = 0; j < Cfg::kSlabsPerWave; ++j) {
-    const uint32_t slab = wave + j * Cfg::kWaves;
-    const uint32_t row = slab * kSlabRows + (lane >> 3);
-    const uint32_t c = (lane & 7u) ^ ((row >> 1) & 7u);  // inverse of chunk_offset's XOR
-    kchunk[j] = c * 8;
-    if (row < static_cast<uint32_t>(BM)) {
-      const int64_t gm = m0 + row;
-      src[j] = gm < args.m ? args.a + gm * args.lda + c * 8 : nullptr;
-    } else {
-      const int64_t gn = n0 + (row - BM);
-      src[j] = gn < args.n ? args.b + gn * args.ldb + c * 8 : nullptr;
-    }
+    const uint32_t row = (wave + j * Cfg::kWaves) * Cfg::kSlabRows + lane / kChunks;
+    const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);  // the XOR is its own inverse
+    if (j < kSlabsA)
+      voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row), last_a)) *
+                     static_cast<uint32_t>(args.lda) + c * 8) * 2;
+    else
+      voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row) - BM, last_b)) *
+                     static_cast<uint32_t>(args.ldb) + c * 8) * 2;
   }
-  const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero_chunk);
+  const char* a_tile = reinterpret_cast<const char*>(args.a + m0 * args.lda);
+  const char* b_tile = reinterpret_cast<const char*>(args.b + n0 * args.ldb);
 
-  auto load_stage = [&](int stage, int k0) {
-    unsigned char* base = smem + stage * Cfg::kStageBytes;
-#pragma unroll
-    for (int j = 0; j < Cfg::kSlabsPerWave; ++j) {
-      const uint32_t slab = wave + j * Cfg::kWaves;
-      const bool in = src[j] != nullptr && static_cast<int>(k0 + kchunk[j]) < args.k;
-      const uint16_t* g = in ? src[j] + k0 : zero;
-      __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(base + slab * 1024u),
-                                       16, 0, 0);
-    }
+  // Copy of slab j of K tile kt into LDS buffer `stage` (whole tile in K).
+  auto dma = [&](int stage, int j, int kt) {
+    const char* base = (j < kSlabsA ? a_tile : b_tile) + static_cast<int64_t>(kt) * Cfg::kRowBytes;
+    // (the builtin takes a non-const global pointer; it only reads it)
+    __builtin_amdgcn_global_load_lds(
+        const_cast<char*>(base + voff[j]),
+        (lds_void_ptr)(smem + stage * Cfg::kStageBytes + (wave + j * Cfg::kWaves) * kDmaBytes),
+        16, 0, 0);
+  };
+  // The same for the last K tile when K is not a multiple of BK: chunks at
+  // or past K come from the zero block (K is a multiple of 8, so a chunk is
+  // wholly inside or wholly outside).
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero_chunk);
+  auto dma_tail = [&](int stage, int j, int kt) {
+    const uint32_t row = (wave + j * Cfg::kWaves) * Cfg::kSlabRows + lane / kChunks;
+    const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);
+    const int k = kt * Cfg::BK + static_cast<int>(c) * 8;
+    const char* base = (j < kSlabsA ? a_tile : b_tile) + static_cast<int64_t>(kt) * Cfg::kRowBytes;
+    const void* g = k < args.k ? static_cast<const void*>(base + voff[j])
+                               : static_cast<const void*>(zero);
+    __builtin_amdgcn_global_load_lds(
+        const_cast<void*>(g), (lds_void_ptr)(smem + stage * Cfg::kStageBytes + (wave + j * Cfg::kWaves) * kDmaBytes),
+        16, 0, 0);
   };
 
   f32x16 acc[Cfg::kFragM][Cfg::kFragN];
@@ -239,34 +328,90 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 
   const uint32_t wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const uint32_t frag_row = lane & 31u, frag_half = lane >> 5;
-  const int ktiles = (args.k + kBK - 1) / kBK;
+  const int ktiles = (args.k + Cfg::BK - 1) / Cfg::BK;
+  const int kfull = args.k / Cfg::BK;  // K tiles with no chunk past K
+  constexpr int kSteps = Cfg::BK / 16;  // MFMA steps per K tile
+  constexpr int kDmaPerStep = (Cfg::kSlabsPerWave + kSteps - 1) / kSteps;
 
-  if (ktiles > 0) load_stage(0, 0);
-  for (int kt = 0; kt < ktiles; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this stage's copies have landed
-    __syncthreads();                     // ... for every wave; the other stage is free
-    if (kt + 1 < ktiles) load_stage((kt + 1) & 1, (kt + 1) * kBK);
-    const unsigned char* sa = smem + (kt & 1) * Cfg::kStageBytes;
-    const unsigned char* sb = sa + BM * kRowBytes;
+  // Ring of STAGES buffers: tile kt lives in buffer kt % STAGES, and the
+  // copies of tile kt + STAGES - 1 are issued while tile kt is multiplied,
+  // spread over its MFMA steps. Fragments are read one step ahead.
+  int cur = 0;                     // buffer of tile kt
+  int fill = Cfg::STAGES - 1;      // buffer of tile kt + STAGES - 1
+  bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
+
+  // LOAD: 0 = no copies, 1 = whole tile, 2 = the partial last tile
+  auto tile_body = [&](int kt, auto load_c) {
+    constexpr int LOAD = decltype(load_c)::value;
+    // Tile kt has landed once at most the copies of the tiles after it are
+    // outstanding (vmcnt counts this lane's DMAs in issue order).
+    if (kt + Cfg::STAGES - 2 < ktiles)
+      wait_vmcnt<(Cfg::STAGES - 2) * Cfg::kSlabsPerWave>();
+    else
+      wait_vmcnt<0>();
+    barrier_lds();  // every wave's copies are visible; buffer `fill` is free
+    const int next = kt + Cfg::STAGES - 1;
+    if constexpr (LOAD == 2) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+      for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(fill, j, next);
+    }
+    const unsigned char* sa = smem + cur * Cfg::kStageBytes;
+    const unsigned char* sb = sa + BM * Cfg::kRowBytes;
+    auto read_frags = [&](int kk, int buf) {
       const uint32_t c = 2 * kk + frag_half;
-      bf16x8 fa[Cfg::kFragM], fb[Cfg::kFragN];
 #pragma unroll
       for (int i = 0; i < Cfg::kFragM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(
-            sa + chunk_offset(wm * Cfg::WM + i * 32 + frag_row, c));
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(
+            sa + Cfg::chunk_offset(wm * Cfg::WM + i * 32 + frag_row, c));
 #pragma unroll
       for (int j = 0; j < Cfg::kFragN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(
-            sb + chunk_offset(wn * Cfg::WN + j * 32 + frag_row, c));
+        fb[buf][j] = *reinterpret_cast<const bf16x8*>(
+            sb + Cfg::chunk_offset(wn * Cfg::WN + j * 32 + frag_row, c));
+    };
+    if constexpr (kPrefetch) read_frags(0, 0);
+    if constexpr (kSchedule) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, Cfg::kFragM + Cfg::kFragN, 0);
+    static_for<kSteps>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      if constexpr (!kPrefetch) read_frags(kk, kk & 1);
+      else if constexpr (kk + 1 < kSteps) read_frags(kk + 1, (kk + 1) & 1);
+      if constexpr (LOAD == 1) {
+#pragma unroll
+        for (int d = 0; d < kDmaPerStep; ++d)
+          if (kk * kDmaPerStep + d < Cfg::kSlabsPerWave) dma(fill, kk * kDmaPerStep + d, next);
+      }
 #pragma unroll
       for (int i = 0; i < Cfg::kFragM; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
+                                                               acc[i][j], 0, 0, 0);
+      if constexpr (kSchedule) schedule_step<Cfg, kk, kSteps, LOAD == 1 ? kDmaPerStep : 0>();
+    });
+    cur = cur + 1 == Cfg::STAGES ? 0 : cur + 1;
+    fill = fill + 1 == Cfg::STAGES ? 0 : fill + 1;
+  };
+
+#pragma unroll
+  for (int s = 0; s < Cfg::STAGES - 1; ++s) {
+    if (s < kfull) {
+#pragma unroll
+      for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma(s, j, s);
+    } else if (s < ktiles) {
+#pragma unroll
+      for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(s, j, s);
     }
   }
+  // Three phases, each a loop over one instance of the body (an if/else of
+  // two instances inside one loop costs registers): copies of whole tiles;
+  // the copy of the partial last tile, if K has one and it was not already
+  // issued by the prologue; no copies.
+  int kt = 0;
+  for (; kt + Cfg::STAGES - 1 < kfull; ++kt) tile_body(kt, std::integral_constant<int, 1>{});
+  if (kfull < ktiles && kt + Cfg::STAGES - 1 == kfull) {
+    tile_body(kt, std::integral_constant<int, 2>{});
+    ++kt;
+  }
+  for (; kt < ktiles; ++kt) tile_body(kt, std::integral_constant<int, 0>{});
 
   // ---- epilogue. acc[i][j] register r of lane l holds C[m][n] with
   // m = row base + l%32 and n = column base + 8*(r/4) + 4*(l/32) + r%4.
@@ -290,8 +435,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   });
 }
 
-using Big = TileCfg<256, 256, 128, 64>;   // 8 waves, 2 per SIMD
-using Small = TileCfg<128, 128, 64, 64>;  // 4 waves, for grids too small for Big
+#ifndef ASR_GEMM_BIG
+#define ASR_GEMM_BIG 256, 256, 128, 64, 32, 4
+#endif
+#ifndef ASR_GEMM_SMALL
+#define ASR_GEMM_SMALL 128, 128, 64, 64, 64, 2
+#endif
+using Big = TileCfg<ASR_GEMM_BIG>;      // 8 waves, 2 per SIMD
+using Small = TileCfg<ASR_GEMM_SMALL>;  // 4 waves, for grids too small for Big
 
 }  // namespace asr_gemm
 
@@ -342,6 +493,9 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb
   if (m == 0 || n == 0) return ok();
   if (!c || (k > 0 && (!a || !b))) return fail(ASR_EINVAL, "gemm: null matrix pointer");
   if (lda < k || ldb < k || ldc < n) return fail(ASR_EINVAL, "gemm: lda, ldb >= k and ldc >= n");
+  // the copies address a tile's rows by 32-bit byte offsets from its first row
+  if (lda >= (int64_t{1} << 23) || ldb >= (int64_t{1} << 23))
+    return fail(ASR_EINVAL, "gemm: lda and ldb must be below 2**23");
   if (k % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0)
     return fail(ASR_EALIGN, "gemm: k, lda and ldb must be multiples of 8");
   if (!aligned_to(a, 16) || !aligned_to(b, 16))
