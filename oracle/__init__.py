@@ -13,6 +13,8 @@ Sources (the pages are cited by title and section):
   * The same FlyDSL page, GEMM and Tests sections: a bf16 GEMM whose f32
     accumulator is rounded to bf16 by RN or by SR keyed per output element
     (oracle/gemm.py).
+  * The same FlyDSL page, discussion section: the generator as a general
+    random-number facility (dropout, initialisation) -- oracle/rng.py.
   * "adamw-sr" (kernels hub page), intro, Usage, Method, Correctness sections:
     the decoupled-weight-decay AdamW step, fp32 states, bf16 write-back by
     stochastic rounding, random bits tied to the key (seed, step) and to
@@ -54,3 +56,4 @@ from .gemm import (  # noqa: F401,E402
     gemm_exact, gemm_exact_scalar, gemm_dot, abs_products, f32_sum_bound,
     gemm_round, gemm_round_at,
 )
+from . import rng  # noqa: F401,E402
