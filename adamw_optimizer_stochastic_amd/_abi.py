@@ -16,7 +16,7 @@ from ._build import LIB_PATH
 ASR_OK, ASR_EINVAL, ASR_EDTYPE, ASR_EALIGN, ASR_EWORKSPACE, ASR_EHIP = range(6)
 ASR_F32, ASR_BF16 = 0, 1
 ASR_ROUND_SR, ASR_ROUND_RN = 0, 1
-ABI_VERSION = 101
+ABI_VERSION = 102
 
 STATUS_NAMES = {ASR_OK: "ASR_OK", ASR_EINVAL: "ASR_EINVAL", ASR_EDTYPE: "ASR_EDTYPE",
                 ASR_EALIGN: "ASR_EALIGN", ASR_EWORKSPACE: "ASR_EWORKSPACE",
@@ -58,6 +58,15 @@ _SIGNATURES = {
                                        _c.c_uint32, _c.c_uint64, _c.c_void_p]),
     "asr_cvt_f32_bf16_rn": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "asr_f32_sqrt_div": (_c.c_int, [_c.c_void_p] * 4 + [_c.c_int64, _c.c_void_p]),
+    "asr_random_uniform": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int64, _c.c_double,
+                                      _c.c_double, _c.c_uint32, _c.c_uint32, _c.c_uint64,
+                                      _c.c_void_p]),
+    "asr_random_normal": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int64, _c.c_double,
+                                     _c.c_double, _c.c_uint32, _c.c_uint32, _c.c_uint64,
+                                     _c.c_void_p]),
+    "asr_dropout": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int64,
+                               _c.c_double, _c.c_uint32, _c.c_uint32, _c.c_uint64,
+                               _c.c_void_p]),
     "asr_gemm_bf16": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                  _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
                                  _c.c_int32, _c.c_uint32, _c.c_uint32, _c.c_uint64,
@@ -157,6 +166,21 @@ def asr_gemm_bf16(a, lda, b, ldb, c, ldc, c_f32, m, n, k, rounding, seed, step, 
                   stream):
     _check(lib().asr_gemm_bf16(a, lda, b, ldb, c, ldc, c_f32, m, n, k, rounding, seed, step,
                                base_index, stream), "asr_gemm_bf16")
+
+
+def asr_random_uniform(out, dtype, n, low, high, seed, step, base_index, stream):
+    _check(lib().asr_random_uniform(out, dtype, n, low, high, seed, step, base_index, stream),
+           "asr_random_uniform")
+
+
+def asr_random_normal(out, dtype, n, mean, std, seed, step, base_index, stream):
+    _check(lib().asr_random_normal(out, dtype, n, mean, std, seed, step, base_index, stream),
+           "asr_random_normal")
+
+
+def asr_dropout(x, y, mask, dtype, n, p, seed, step, base_index, stream):
+    _check(lib().asr_dropout(x, y, mask, dtype, n, p, seed, step, base_index, stream),
+           "asr_dropout")
 
 
 def asr_sr_bf16_given_bits(x, r16, out, n, stream):

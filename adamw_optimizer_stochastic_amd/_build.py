@@ -1,8 +1,9 @@
 """Build step: compiles the HIP sources into the in-tree shared library.
 
-Two translation units (csrc/adamw_sr.hip: the AdamW step, the generator and
-the conversions; csrc/gemm_sr.hip: the GEMM; both include csrc/device.hpp,
-csrc/status.hpp and include/adamw_sr.h) -> libadamw_sr.so, for gfx950 only. Flags that matter
+Three translation units (csrc/adamw_sr.hip: the AdamW step, the generator and
+the conversions; csrc/gemm_sr.hip: the GEMM; csrc/random.hip: uniform/normal
+draws and dropout; all include csrc/device.hpp, csrc/status.hpp and
+include/adamw_sr.h) -> libadamw_sr.so, for gfx950 only. Flags that matter
 for the arithmetic:
   -ffp-contract=off                          no fused multiply-adds (the
                                              sources also say so by pragma)
@@ -22,7 +23,8 @@ import tempfile
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 SOURCES = [os.path.join(PKG_DIR, "csrc", "adamw_sr.hip"),
-           os.path.join(PKG_DIR, "csrc", "gemm_sr.hip")]
+           os.path.join(PKG_DIR, "csrc", "gemm_sr.hip"),
+           os.path.join(PKG_DIR, "csrc", "random.hip")]
 DEPENDS = SOURCES + [os.path.join(PKG_DIR, "csrc", "device.hpp"),
                      os.path.join(PKG_DIR, "csrc", "status.hpp"),
                      os.path.join(ROOT, "include", "adamw_sr.h")]

@@ -172,6 +172,34 @@ def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, ou
     return out
 
 
+class RoundingMode:
+    """Rounding modes of the f32 -> bf16 conversion ("Add stochastic rounding
+    and philox RNG helpers", discussion: stochastic rounding as a rounding
+    mode of the existing conversion, keyed by a seed)."""
+    NEAREST = "rn"
+    STOCHASTIC = "sr"
+
+
+def to(x, dtype=torch.bfloat16, *, rounding=RoundingMode.NEAREST, seed=0, step=0, base_index=0,
+       out=None):
+    """x.to(dtype) with a choice of rounding, for float32 -> bfloat16.
+
+    rounding NEAREST: round to nearest even. STOCHASTIC: element i uses the
+    16 random bits of stream position base_index + i under key (seed, step)
+    (asr_cvt_f32_bf16_sr). Any shape; x must be contiguous float32 on a GPU.
+    A float32 -> float32 request returns x itself.
+    """
+    if dtype == x.dtype == torch.float32:
+        return x
+    if dtype != torch.bfloat16:
+        raise NotImplementedError("to(): float32 -> bfloat16 only")
+    if rounding in (RoundingMode.STOCHASTIC, "sr", "stochastic"):
+        return cvt_f32_bf16_sr(x, seed, step, base_index, out=out)
+    if rounding in (RoundingMode.NEAREST, "rn", "nearest"):
+        return cvt_f32_bf16_rn(x, out=out)
+    raise ValueError(f"unknown rounding {rounding!r}")
+
+
 def f32_sqrt_div(a, b):
     """(sqrt(a), a / b) as the AdamW kernel evaluates them (test support)."""
     for t, name in ((a, "a"), (b, "b")):

@@ -8,7 +8,7 @@ in HBM), the dominant kernel's achieved HBM bandwidth against the 8 TB/s
 peak (algorithmic bytes: 22 per element), and the CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|shards|convert|gemm]
+    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|shards|convert|gemm|rng]
     python bench.py --copy-probe      # plain copy of known size (counter scaling)
 
 The gemm workload times the bf16 GEMM with the SR epilogue on the gate/up
@@ -296,6 +296,54 @@ def run_gemm(args, torch, ops, wl):
     }
 
 
+def run_rng(args, torch, ops, wl):
+    """Dropout over 2**30 f32 elements with its keep mask (read 4 B, write
+    4 + 1 B per element: HBM-bound), with normal and uniform fills of the
+    same size timed beside it."""
+    from adamw_optimizer_stochastic_amd import random as arng
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.float32, device=dev)
+    arng.normal_(x, seed=1, step=0)
+    y = torch.empty_like(x)
+    mask = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    from adamw_optimizer_stochastic_amd import _abi
+
+    def drop():
+        _abi.asr_dropout(x.data_ptr(), y.data_ptr(), mask.data_ptr(), _abi.ASR_F32, n, 0.1, 2, 0,
+                         0, stream.cuda_stream)
+
+    def normal():
+        arng.normal_(y, seed=3, step=1)
+
+    def uniform():
+        arng.uniform_(y, seed=3, step=1)
+
+    for fn in (drop, normal, uniform):
+        for _ in range(args.warmup):
+            fn()
+    wall, drop_ms = _time_launches(torch, stream, drop, args.steps)
+    _, normal_ms = _time_launches(torch, stream, normal, args.steps)
+    _, uniform_ms = _time_launches(torch, stream, uniform, args.steps)
+    achieved = 9 * n / (drop_ms * 1e-3) / 1e9
+    return {
+        "metric": "elements/sec, Philox dropout with keep mask, 1 GPU", "value": n / wall,
+        "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "dropout_2^30_f32_p0.1", "algorithmic_bytes_per_element": 9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "asr_rng::rng_kernel<dropout, f32>", "kernel_ms_avg": drop_ms},
+        "context": {"normal_fill_ms": normal_ms,
+                    "normal_fill_GBps": 4 * n / (normal_ms * 1e-3) / 1e9,
+                    "uniform_fill_ms": uniform_ms,
+                    "uniform_fill_GBps": 4 * n / (uniform_ms * 1e-3) / 1e9},
+    }
+
+
 def run_copy_probe(args, torch):
     """A plain device copy of 8 GiB (torch's copy kernel), for scaling the
     FETCH_SIZE/WRITE_SIZE counters: it moves exactly 8 GiB each way."""
@@ -320,7 +368,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "shards", "convert", "gemm"])
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "shards", "convert", "gemm", "rng"])
     ap.add_argument("--gemm-shape", default=None, help="M,N,K for --workload gemm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -357,6 +405,8 @@ def main():
         res = run_convert(args, torch, ops, wl)
     elif args.workload == "gemm":
         res = run_gemm(args, torch, ops, wl)
+    elif args.workload == "rng":
+        res = run_rng(args, torch, ops, wl)
     else:
         res = run_adamw(args, torch, ops, wl)
     if cpu is not None:

@@ -229,6 +229,49 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b,
                   void* stream);
 
 /*
+ * Random numbers on the library's stream, beyond rounding.
+ * ("Add stochastic rounding and philox RNG helpers", discussion: the
+ * counter-based generator as a general facility for dropout and
+ * initialisation; "adamw-sr", Method: keyed by (seed, step), indexed by the
+ * global position of the element.)
+ * Position p = base_index + i takes 32-bit word W = word p & 3 of the
+ * Philox4x32-10 call with counter (lo32(p >> 2), hi32(p >> 2), 0, 0) and key
+ * (seed, step) -- the stream asr_philox_4x32_fill writes. All arithmetic is
+ * binary32 without contraction; an ASR_BF16 output is the round-to-nearest-
+ * even of the binary32 value. A tensor split into pieces that each pass
+ * their own base_index reproduces the whole bit for bit.
+ *
+ * asr_random_uniform: out[i] = f32(low) + f32(high - low) * U,
+ *   U = (W >> 8) * 2**-24 in [0, 1). low, high finite.
+ * asr_random_normal: Box-Muller on position pairs (2q, 2q + 1):
+ *   u1 = ((W(2q) >> 8) + 1) * 2**-24, u2 = (W(2q + 1) >> 8) * 2**-24,
+ *   r = sqrt(-2 ln u1); z(2q) = r cos(2 pi u2), z(2q + 1) = r sin(2 pi u2);
+ *   out[i] = f32(mean) + f32(std) * z. log, sin and cos are the device
+ *   library's binary32 functions (a few ulp), so values are reproducible on
+ *   this library but not bit-identical to other implementations.
+ *   mean finite, std finite and >= 0.
+ * asr_dropout: drop probability p in [0, 1). Element i is dropped when
+ *   W < floor(p * 2**32); y[i] = x[i] * (dropped ? 0 : f32(1 / (1 - p))), one
+ *   binary32 multiply (a dropped Inf or NaN gives NaN, a dropped negative
+ *   value -0). mask: NULL, or n bytes receiving 1 for kept, 0 for dropped.
+ *   x and y may be the same buffer (in place).
+ *
+ * out, x, y: device, n elements of dtype (ASR_F32 or ASR_BF16), aligned to
+ * the element size (16-byte f32 / 8-byte bf16 alignment takes the vector
+ * path). Errors: ASR_EDTYPE, ASR_EINVAL (sizes, parameters, NULL),
+ * ASR_EALIGN, ASR_EHIP. Run on `stream`; do not synchronize.
+ */
+int asr_random_uniform(void* out, int32_t dtype, int64_t n, double low,
+                       double high, uint32_t seed, uint32_t step,
+                       uint64_t base_index, void* stream);
+int asr_random_normal(void* out, int32_t dtype, int64_t n, double mean,
+                      double std, uint32_t seed, uint32_t step,
+                      uint64_t base_index, void* stream);
+int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype,
+                int64_t n, double p, uint32_t seed, uint32_t step,
+                uint64_t base_index, void* stream);
+
+/*
  * Test support: the binary32 square root and division exactly as the AdamW
  * kernel evaluates them: sqrt_out[i] = sqrt(a[i]), div_out[i] = a[i] / b[i],
  * both correctly rounded (to nearest even, subnormals kept).
@@ -245,7 +288,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 101
+#define ASR_ABI_VERSION 102
 
 #ifdef __cplusplus
 }

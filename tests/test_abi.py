@@ -182,3 +182,29 @@ def test_gemm_argument_errors():
     assert g(m=0, a=0, b=0, c=0) == E.ASR_OK
     assert g(n=0, a=0, b=0, c=0) == E.ASR_OK
     assert _abi.asr_last_error() == ""
+
+
+def test_random_argument_errors():
+    """Every check of the random-number entry points returns before the
+    first HIP call."""
+    E = _abi
+    u, nrm, d = _abi.asr_random_uniform, _abi.asr_random_normal, _abi.asr_dropout
+    assert _status(u, 0x1000, 7, 16, 0.0, 1.0, 1, 2, 0, None) == E.ASR_EDTYPE
+    assert _status(u, 0x1000, E.ASR_F32, -1, 0.0, 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(u, 0, E.ASR_F32, 16, 0.0, 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(u, 0x1002, E.ASR_F32, 16, 0.0, 1.0, 1, 2, 0, None) == E.ASR_EALIGN
+    assert _status(u, 0x1001, E.ASR_BF16, 16, 0.0, 1.0, 1, 2, 0, None) == E.ASR_EALIGN
+    assert _status(u, 0x1000, E.ASR_F32, 16, float("inf"), 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(u, 0x1000, E.ASR_F32, 16, -1e308, 1e308, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(nrm, 0x1000, E.ASR_F32, 16, 0.0, -1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(nrm, 0x1000, E.ASR_F32, 16, float("nan"), 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(d, 0x1000, 0x2000, None, E.ASR_F32, 16, 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(d, 0x1000, 0x2000, None, E.ASR_F32, 16, -0.1, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(d, 0x1000, 0x2000, None, E.ASR_F32, 16, float("nan"), 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(d, 0, 0x2000, None, E.ASR_F32, 16, 0.5, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(d, 0x1002, 0x2000, None, E.ASR_F32, 16, 0.5, 1, 2, 0, None) == E.ASR_EALIGN
+    # nothing to do
+    assert _status(u, 0, E.ASR_F32, 0, 0.0, 1.0, 1, 2, 0, None) == E.ASR_OK
+    assert _status(nrm, 0, E.ASR_BF16, 0, 0.0, 1.0, 1, 2, 0, None) == E.ASR_OK
+    assert _status(d, 0, 0, None, E.ASR_BF16, 0, 0.5, 1, 2, 0, None) == E.ASR_OK
+    assert _abi.asr_last_error() == ""

@@ -1,0 +1,171 @@
+"""Random numbers beyond rounding (asr_random_uniform, asr_random_normal,
+asr_dropout) and the to() conversion surface, against the oracle.
+
+Uniform draws and dropout are integer decisions and exact binary32
+operations on the stream words: bit-exact. Normal draws go through the
+device library's log and sincos: compared with the oracle's binary64 value
+within 2**-20 * (std * r + |mean| + |y|), r the pair's radius. That covers
+a radius error of about 2**-22 relative (log within 2 ulp, a correctly
+rounded sqrt), sincos within 2 ulp, and the rounding of the final multiply
+and add, with a factor-of-two margin. The bf16 form must be the
+round-to-nearest of the kernel's own f32 value.
+Sizes cover one element, ragged tails, several workgroups and unaligned
+starting positions (a pair split across pieces for the normal draws).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import rng as orng
+from adamw_optimizer_stochastic_amd import random as arng, ops, RoundingMode, to
+from _gpu_util import (gpu, require_gpu, announce, to_host, assert_bits_equal, f32_tensor,
+                       bf16_tensor)
+
+pytestmark = gpu
+
+SIZES = [1, 3, 1023, 1025, 65537, (1 << 20) + 3]
+BASES = [0, 1, 2, 3, (1 << 40) + 5]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("base", BASES)
+def test_uniform_bit_exact(n, base):
+    announce("uniform", n, base)
+    seed, step = 1234, 5
+    for low, high in ((0.0, 1.0), (-2.5, 7.25)):
+        got = arng.uniform(n, low, high, seed=seed, step=step, base_index=base)
+        want = orng.uniform_f32(n, seed, step, base, low, high)
+        assert_bits_equal(to_host(got), want, f"uniform f32 n={n} base={base}")
+        gotb = arng.uniform(n, low, high, seed=seed, step=step, base_index=base,
+                            dtype=torch.bfloat16)
+        assert_bits_equal(to_host(gotb), oracle.rn_bf16(oracle.f32_bits(want)),
+                          f"uniform bf16 n={n} base={base}")
+
+
+def test_uniform_pieces_reproduce_whole():
+    announce("uniform pieces")
+    n = 300001
+    whole = to_host(arng.uniform(n, seed=9, step=2, base_index=10))
+    cuts = [0, 1, 4099, 77777, 200002, n]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        part = to_host(arng.uniform(b - a, seed=9, step=2, base_index=10 + a))
+        assert np.array_equal(part.view(np.uint32), whole[a:b].view(np.uint32))
+
+
+def _normal_bound(y64, r, mean, std):
+    # |z_f32 - z| <= r * 2**-21 (radius and sincos errors), then the binary32
+    # multiply-add: half an ulp of |std z| and of |y| each, with slack
+    return 2.0 ** -20 * (abs(std) * r + abs(mean) + np.abs(y64)) + 1e-30
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("base", [0, 1, 3, (1 << 40) + 5])
+def test_normal_within_bound(n, base):
+    announce("normal", n, base)
+    seed, step = 77, 3
+    for mean, std in ((0.0, 1.0), (1.5, 0.02)):
+        got = to_host(arng.normal(n, mean, std, seed=seed, step=step, base_index=base))
+        y64, r = orng.normal_f64(n, seed, step, base, mean, std)
+        err = np.abs(got.astype(np.float64) - y64)
+        bound = _normal_bound(y64, r, mean, std)
+        assert np.all(err <= bound), f"max err/bound {np.max(err / bound)}"
+        gotb = to_host(arng.normal(n, mean, std, seed=seed, step=step, base_index=base,
+                                   dtype=torch.bfloat16))
+        assert_bits_equal(gotb, oracle.rn_bf16(oracle.f32_bits(got)), "normal bf16 = rn(f32)")
+
+
+def test_normal_pieces_and_statistics():
+    announce("normal pieces/stats")
+    n = 1 << 22
+    whole = to_host(arng.normal(n, seed=5, step=1, base_index=3))
+    part = to_host(arng.normal(n - 1001, seed=5, step=1, base_index=3 + 1001))  # odd cut
+    assert np.array_equal(part.view(np.uint32), whole[1001:].view(np.uint32))
+    z = whole.astype(np.float64)
+    assert abs(z.mean()) < 5 / np.sqrt(n)
+    assert abs(z.var() - 1) < 5 * np.sqrt(2 / n)
+
+
+SPECIALS = np.array([np.inf, -np.inf, np.nan, -3.0, 0.0, -0.0, 1e-40, 3.4e38], dtype=np.float32)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.5, 0.9, 0.999])
+@pytest.mark.parametrize("n,base", [(1, 0), (1023, 1), (65537, 2), ((1 << 20) + 3, (1 << 40) + 5)])
+def test_dropout_bit_exact(p, n, base):
+    announce("dropout", p, n, base)
+    g = np.random.default_rng(n)
+    x = g.standard_normal(n).astype(np.float32)
+    x[: min(n, SPECIALS.size)] = SPECIALS[: min(n, SPECIALS.size)]
+    seed, step = 31, 8
+    y, mask = arng.dropout(f32_tensor(x), p, seed=seed, step=step, base_index=base,
+                           return_mask=True)
+    wy, wk = orng.dropout_f32(x, p, seed, step, base)
+    assert_bits_equal(to_host(y), wy, f"dropout f32 p={p}")
+    assert np.array_equal(to_host(mask.view(torch.uint8)).astype(bool), wk)
+    xb = oracle.rn_bf16(oracle.f32_bits(x)).astype(np.uint16)
+    yb = arng.dropout(bf16_tensor(xb), p, seed=seed, step=step, base_index=base)
+    wyb, _ = orng.dropout_bf16(xb, p, seed, step, base)
+    assert_bits_equal(to_host(yb), wyb, f"dropout bf16 p={p}")
+
+
+def test_dropout_in_place_and_eval():
+    announce("dropout in place")
+    x = np.linspace(-3, 3, 4099, dtype=np.float32)
+    t = f32_tensor(x)
+    want, _ = orng.dropout_f32(x, 0.3, 4, 4, 0)
+    out = arng.dropout(t, 0.3, seed=4, step=4, inplace=True)
+    assert out.data_ptr() == t.data_ptr()
+    assert_bits_equal(to_host(t), want, "in place")
+    same = arng.dropout(t, 0.3, seed=4, step=4, training=False)
+    assert same is t
+
+
+def test_to_surface():
+    announce("to()")
+    g = np.random.default_rng(2)
+    x = g.standard_normal((37, 129)).astype(np.float32)
+    t = f32_tensor(x)
+    rn = to(t, torch.bfloat16)
+    assert rn.shape == t.shape and rn.dtype == torch.bfloat16
+    assert_bits_equal(to_host(rn).reshape(-1), oracle.cvt_f32_bf16_rn(x), "to rn")
+    sr = to(t, torch.bfloat16, rounding=RoundingMode.STOCHASTIC, seed=3, step=1, base_index=11)
+    assert_bits_equal(to_host(sr).reshape(-1), oracle.cvt_f32_bf16_sr(x, 3, 1, 11), "to sr")
+    assert to(t, torch.float32) is t
+    with pytest.raises(NotImplementedError):
+        to(t, torch.float16)
+
+
+def test_full_size_sampled():
+    """Dropout and normal draws over 2**30 elements in the launch
+    configuration the benchmark times; sampled positions against the oracle."""
+    announce("rng full size 2**30")
+    n = 1 << 30
+    dev = torch.device("cuda", 0)
+    x = torch.empty(n, dtype=torch.float32, device=dev)
+    arng.normal_(x, seed=1, step=0)
+    idx = np.unique(np.concatenate([np.random.default_rng(0).integers(0, n, 4096),
+                                    [0, 1, 2, 3, n - 4, n - 3, n - 2, n - 1]]))
+    xi = to_host(x[torch.from_numpy(idx).to(dev)])
+    # each sampled element on its own: the oracle at base = its position
+    y64 = np.array([orng.normal_f64(1, 1, 0, int(i))[0][0] for i in idx])
+    r = np.array([orng.normal_f64(1, 1, 0, int(i))[1][0] for i in idx])
+    assert np.all(np.abs(xi.astype(np.float64) - y64) <= _normal_bound(y64, r, 0.0, 1.0))
+    y = torch.empty_like(x)
+    mask = torch.empty(n, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        from adamw_optimizer_stochastic_amd import _abi
+        _abi.asr_dropout(x.data_ptr(), y.data_ptr(), mask.data_ptr(), _abi.ASR_F32, n, 0.1, 2, 0,
+                         0, ops._stream(dev))
+    torch.cuda.synchronize()
+    yi = to_host(y[torch.from_numpy(idx).to(dev)])
+    mi = to_host(mask[torch.from_numpy(idx).to(dev)])
+    for k, i in enumerate(idx):
+        wy, wk = orng.dropout_f32(xi[k:k + 1], 0.1, 2, 0, int(i))
+        assert yi[k].view(np.uint32) == wy[0].view(np.uint32) and bool(mi[k]) == bool(wk[0])
+    del x, y, mask
