@@ -55,14 +55,10 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;         // tile rows per group in the tile order
 constexpr int kDmaBytes = 1024;    // LDS bytes one wave-wide 16-byte-per-lane DMA fills
-#ifndef ASR_GEMM_PREFETCH
-#define ASR_GEMM_PREFETCH 1
-#endif
-constexpr bool kPrefetch = ASR_GEMM_PREFETCH;  // read fragments one MFMA step ahead
 #ifndef ASR_GEMM_SCHEDULE
 #define ASR_GEMM_SCHEDULE 1
 #endif
-constexpr bool kSchedule = ASR_GEMM_SCHEDULE && ASR_GEMM_PREFETCH;  // see schedule_step
+constexpr bool kSchedule = ASR_GEMM_SCHEDULE;  // see schedule_step
 
 // Source of chunks outside the matrices (rows past M or N, columns past K).
 __device__ __align__(16) uint4 g_zero_chunk;
@@ -335,57 +331,77 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 
   // Ring of STAGES buffers: tile kt lives in buffer kt % STAGES, and the
   // copies of tile kt + STAGES - 1 are issued while tile kt is multiplied,
-  // spread over its MFMA steps. Fragments are read one step ahead.
+  // spread over its MFMA steps. Fragments are read one step ahead, the
+  // first step's across the tile boundary (see tile_body).
   int cur = 0;                     // buffer of tile kt
   int fill = Cfg::STAGES - 1;      // buffer of tile kt + STAGES - 1
   bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
 
-  // LOAD: 0 = no copies, 1 = whole tile, 2 = the partial last tile
+  // LOAD: 0 = no copies, 1 = whole tile, 2 = the partial last tile.
+  // The barrier sits inside the last MFMA step of each tile.
+  // Half of that step's MFMAs are issued, then the wave waits for tile
+  // kt + 1, passes the barrier and issues tile kt + 1's first fragment
+  // reads, and the other half of the MFMAs cover their latency. The next
+  // tile then starts with its fragments in registers instead of behind a
+  // barrier and a round trip to the LDS.
+  auto read_frags_from = [&](const unsigned char* sa, int kk, int buf) {
+    const unsigned char* sb = sa + BM * Cfg::kRowBytes;
+    const uint32_t c = 2 * kk + frag_half;
+#pragma unroll
+    for (int i = 0; i < Cfg::kFragM; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(
+          sa + Cfg::chunk_offset(wm * Cfg::WM + i * 32 + frag_row, c));
+#pragma unroll
+    for (int j = 0; j < Cfg::kFragN; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8*>(
+          sb + Cfg::chunk_offset(wn * Cfg::WN + j * 32 + frag_row, c));
+  };
+  auto wait_for = [&](int tile) {  // this lane's copies of tile `tile` have landed
+    if (tile + Cfg::STAGES - 2 < ktiles) wait_vmcnt<(Cfg::STAGES - 2) * Cfg::kSlabsPerWave>();
+    else wait_vmcnt<0>();
+  };
   auto tile_body = [&](int kt, auto load_c) {
     constexpr int LOAD = decltype(load_c)::value;
-    // Tile kt has landed once at most the copies of the tiles after it are
-    // outstanding (vmcnt counts this lane's DMAs in issue order).
-    if (kt + Cfg::STAGES - 2 < ktiles)
-      wait_vmcnt<(Cfg::STAGES - 2) * Cfg::kSlabsPerWave>();
-    else
-      wait_vmcnt<0>();
-    barrier_lds();  // every wave's copies are visible; buffer `fill` is free
+    static_assert(kSteps % 2 == 0, "fragment sets alternate per step");
     const int next = kt + Cfg::STAGES - 1;
     if constexpr (LOAD == 2) {
 #pragma unroll
       for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(fill, j, next);
     }
     const unsigned char* sa = smem + cur * Cfg::kStageBytes;
-    const unsigned char* sb = sa + BM * Cfg::kRowBytes;
-    auto read_frags = [&](int kk, int buf) {
-      const uint32_t c = 2 * kk + frag_half;
-#pragma unroll
-      for (int i = 0; i < Cfg::kFragM; ++i)
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(
-            sa + Cfg::chunk_offset(wm * Cfg::WM + i * 32 + frag_row, c));
-#pragma unroll
-      for (int j = 0; j < Cfg::kFragN; ++j)
-        fb[buf][j] = *reinterpret_cast<const bf16x8*>(
-            sb + Cfg::chunk_offset(wn * Cfg::WN + j * 32 + frag_row, c));
-    };
-    if constexpr (kPrefetch) read_frags(0, 0);
-    if constexpr (kSchedule) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, Cfg::kFragM + Cfg::kFragN, 0);
+    const unsigned char* na = smem + (cur + 1 == Cfg::STAGES ? 0 : cur + 1) * Cfg::kStageBytes;
     static_for<kSteps>([&](auto kkc) {
       constexpr int kk = decltype(kkc)::value;
-      if constexpr (!kPrefetch) read_frags(kk, kk & 1);
-      else if constexpr (kk + 1 < kSteps) read_frags(kk + 1, (kk + 1) & 1);
+      if constexpr (kk + 1 < kSteps) read_frags_from(sa, kk + 1, (kk + 1) & 1);
       if constexpr (LOAD == 1) {
 #pragma unroll
         for (int d = 0; d < kDmaPerStep; ++d)
           if (kk * kDmaPerStep + d < Cfg::kSlabsPerWave) dma(fill, kk * kDmaPerStep + d, next);
       }
+      constexpr int kHalf = kk + 1 < kSteps ? Cfg::kFragM : Cfg::kFragM / 2;
 #pragma unroll
-      for (int i = 0; i < Cfg::kFragM; ++i)
+      for (int i = 0; i < kHalf; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::kFragN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
                                                                acc[i][j], 0, 0, 0);
-      if constexpr (kSchedule) schedule_step<Cfg, kk, kSteps, LOAD == 1 ? kDmaPerStep : 0>();
+      if constexpr (kk + 1 < kSteps) {
+        if constexpr (kSchedule) schedule_step<Cfg, kk, kSteps, LOAD == 1 ? kDmaPerStep : 0>();
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < ktiles) {
+          wait_for(kt + 1);
+          barrier_lds();  // tile kt + 1 visible; every wave is done with tile kt - 1's buffer
+          read_frags_from(na, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = kHalf; i < Cfg::kFragM; ++i)
+#pragma unroll
+          for (int j = 0; j < Cfg::kFragN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
+                                                                 acc[i][j], 0, 0, 0);
+      }
     });
     cur = cur + 1 == Cfg::STAGES ? 0 : cur + 1;
     fill = fill + 1 == Cfg::STAGES ? 0 : fill + 1;
@@ -405,6 +421,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   // two instances inside one loop costs registers): copies of whole tiles;
   // the copy of the partial last tile, if K has one and it was not already
   // issued by the prologue; no copies.
+  // Three phases, each a loop over one instance of the body (an if/else of
+  // two instances inside one loop costs registers): copies of whole tiles;
+  // the copy of the partial last tile, if K has one and it was not already
+  // issued by the prologue; no copies.
+  if (ktiles > 0) {
+    wait_for(0);
+    barrier_lds();
+    read_frags_from(smem, 0, 0);
+  }
   int kt = 0;
   for (; kt + Cfg::STAGES - 1 < kfull; ++kt) tile_body(kt, std::integral_constant<int, 1>{});
   if (kfull < ktiles && kt + Cfg::STAGES - 1 == kfull) {
