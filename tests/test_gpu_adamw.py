@@ -299,6 +299,56 @@ def test_optimizer_class_matches_oracle_and_resumes():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_optimizer_param_groups_dtypes_and_roundings():
+    """AdamWSR with three groups -- bf16 params under SR, an f32 param, a bf16
+    param under RN -- each with its own lr and weight decay, one param that
+    misses a step: every param matches the oracle run with its group's
+    hyperparameters, its own step count and base_index = running numel over
+    all groups."""
+    announce("AdamWSR groups")
+    rng = wl.host_rng(wl.CFG_SMALL, 77)
+    specs = [(0, BF16, 3000), (0, BF16, 1025), (1, F32, 4099), (2, BF16, 777)]
+    groups_hp = [dict(lr=1e-3, weight_decay=0.01, rounding="sr"),
+                 dict(lr=5e-4, weight_decay=0.0, rounding="sr"),
+                 dict(lr=2e-3, weight_decay=0.1, rounding="rn")]
+    params, host = [], []
+    for g, dt, n in specs:
+        x = _host_tensor(rng, n, dt, 0.05)
+        params.append(torch.nn.Parameter(_to_dev(x, dt)))
+        host.append([x, np.zeros(n, np.float32), np.zeros(n, np.float32)])
+    opt = AdamWSR([dict(params=[p for p, (g, _, _) in zip(params, specs) if g == k], **groups_hp[k])
+                   for k in range(3)], betas=(0.9, 0.95), eps=1e-6, seed=11)
+    bases = np.cumsum([0] + [n for _, _, n in specs])[:-1]
+    steps = [0] * len(params)
+    for it in range(4):
+        grads = []
+        for k, (g, dt, n) in enumerate(specs):
+            if it == 2 and k == 1:
+                params[k].grad = None
+                grads.append(None)
+                continue
+            gx = _host_tensor(rng, n, dt, 1e-2)
+            params[k].grad = _to_dev(gx, dt)
+            grads.append(gx)
+        opt.step()
+        for k, (g, dt, n) in enumerate(specs):
+            if grads[k] is None:
+                continue
+            steps[k] += 1
+            hp = groups_hp[g]
+            h = host[k]
+            h[0], h[1], h[2] = oracle.step_tensor(
+                h[0], grads[k], h[1], h[2], param_dtype=dt, grad_dtype=dt,
+                base_index=int(bases[k]), lr=hp["lr"], beta1=0.9, beta2=0.95, eps=1e-6,
+                weight_decay=hp["weight_decay"], step=steps[k], seed=11,
+                rounding=ROUND_SR if hp["rounding"] == "sr" else ROUND_RN)
+    for k, (g, dt, n) in enumerate(specs):
+        st = opt.state[params[k]]
+        _check_outputs((params[k].detach(), st["exp_avg"], st["exp_avg_sq"]), host[k], dt,
+                       f"group {g} param {k}")
+        assert int(st["step"].item()) == steps[k]
+
+
 def test_optimizer_rejects_unsupported_options():
     with pytest.raises(NotImplementedError):
         AdamWSR([torch.zeros(4, device="cuda", requires_grad=True)], amsgrad=True)
