@@ -53,7 +53,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int kXcds = 8;
-constexpr int kGroupM = 4;         // tile rows per group in the tile order
+#ifndef ASR_GEMM_GROUP_M
+#define ASR_GEMM_GROUP_M 4
+#endif
+constexpr int kGroupM = ASR_GEMM_GROUP_M;  // tile rows per group in the tile order
 constexpr int kDmaBytes = 1024;    // LDS bytes one wave-wide 16-byte-per-lane DMA fills
 #ifndef ASR_GEMM_SCHEDULE
 #define ASR_GEMM_SCHEDULE 1
