@@ -350,6 +350,27 @@ convert_f32_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64
   }
 }
 
+// ------------------------------------------------- measurement: a copy
+// A plain copy built like the step: one slot of kBlock lanes x 4 x 16 bytes
+// per workgroup, no loop, 128-bit loads and stores, the same XCD windows and
+// residency cap. It measures what this launch structure gets from HBM for
+// a 1:1 read/write stream, the reference the step's bandwidth is also
+// quoted against.
+constexpr int kCopyVec = 4;  // 16-byte units per lane, one wave-wide 1 KiB access each
+__global__ void __launch_bounds__(kBlock)
+stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16,
+            uint64_t slot0) {
+  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kBlock * kCopyVec) +
+                        threadIdx.x;
+  u32x4 x[kCopyVec];
+#pragma unroll
+  for (int k = 0; k < kCopyVec; ++k)
+    if (base + k * kBlock < n16) x[k] = src[base + k * kBlock];
+#pragma unroll
+  for (int k = 0; k < kCopyVec; ++k)
+    if (base + k * kBlock < n16) dst[base + k * kBlock] = x[k];
+}
+
 // ---------------------------------------------- SR with caller's bits
 // out[i] = SR(x[i], r16[i]): the rounding with its random bits supplied.
 __global__ void __launch_bounds__(kBlock)
@@ -816,6 +837,28 @@ int asr_cvt_f32_bf16_sr(const float* in, uint16_t* out, int64_t n, uint32_t seed
 
 int asr_cvt_f32_bf16_rn(const float* in, uint16_t* out, int64_t n, void* stream) {
   return convert(ASR_ROUND_RN, in, out, n, 0, 0, 0, stream);
+}
+
+int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream_ptr) {
+  if (bytes < 0) return fail(ASR_EINVAL, "bytes < 0");
+  if (bytes == 0) return ok();
+  if (!dst || !src) return fail(ASR_EINVAL, "NULL buffer");
+  if (bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
+    return fail(ASR_EALIGN, "buffers and size must be multiples of 16 bytes");
+  const uint64_t n16 = static_cast<uint64_t>(bytes) / 16;
+  const uint64_t per_slot = static_cast<uint64_t>(asr::kBlock) * asr::kCopyVec;
+  const uint64_t n_slots = (n16 + per_slot - 1) / per_slot;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  uint32_t lds = 0;
+  hipError_t e = occupancy_lds(reinterpret_cast<const void*>(asr::stream_copy), &lds);
+  if (e != hipSuccess) return hip_fail(e, "copy attribute");
+  for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
+    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
+    e = launch_lds(asr::stream_copy, grid, lds, stream, static_cast<const asr::u32x4*>(src),
+                   static_cast<asr::u32x4*>(dst), n16, slot0);
+    if (e != hipSuccess) return hip_fail(e, "copy launch");
+  }
+  return ok();
 }
 
 int asr_sr_bf16_given_bits(const float* x, const uint16_t* r16, uint16_t* out, int64_t n,

@@ -68,20 +68,26 @@ def _oracle_shard(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(per_core=1 << 21):
+def cpu_baseline(per_core=1 << 22):
     """The oracle (numpy, unmodified) on `cores` shards of `per_core` bf16
     elements each, one process per core, before the GPU is touched (the pool
-    forks a process that has not initialised the GPU)."""
+    forks a process that has not initialised the GPU). Each shard times its
+    own step (input generation excluded); the shards run concurrently, so
+    the whole-host rate is the sum of the per-core rates."""
     cores = max(1, min(16, os.cpu_count() or 1))
     ctx = multiprocessing.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(cores) as pool:
-        pool.map(_oracle_shard, [(k, per_core) for k in range(cores)])
+        times = pool.map(_oracle_shard, [(k, per_core) for k in range(cores)])
     wall = time.perf_counter() - t0
+    rates = sorted(per_core / t for t in times)
     n = cores * per_core
-    return {"value": n / wall, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} bf16 params ({cores} shards of {per_core}) of the same workload, "
-                      f"one AdamW-SR step, numpy oracle; wall {wall:.2f} s"}
+    return {"value": sum(rates), "unit": "params/s", "cores": cores, "kind": "oracle",
+            "one_core_value": rates[len(rates) // 2],
+            "sample": f"{n} bf16 params ({cores} concurrent shards of {per_core}) of the same "
+                      f"workload, one AdamW-SR step each, numpy oracle; step times "
+                      f"{min(times):.2f}-{max(times):.2f} s ({sum(times):.1f} CPU-s), "
+                      f"wall with input generation {wall:.1f} s"}
 
 
 # ------------------------------------------------------------- GPU legs
@@ -140,9 +146,11 @@ def run_adamw(args, torch, ops, wl):
     launch_ms = [a.elapsed_time(b) for a, b in events]
     ms_per_step = wall * 1e3 / args.steps
     kernel_ms = sum(launch_ms) / len(launch_ms)
+    kernel_ms_median = sorted(launch_ms)[len(launch_ms) // 2]
     bytes_per_launch = 22 * n_elems
     achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(args.workload, n_elems)
+    copy_gbps = stream_copy_gbps(torch, dev, stream)
     return {
         "metric": METRIC, "value": n_elems / (ms_per_step * 1e-3), "unit": "params/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -156,9 +164,12 @@ def run_adamw(args, torch, ops, wl):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "adamw_sr_class<BF16,BF16,SR> (one launch per size class) + "
                                "adamw_sr_slots<BF16,BF16,SR> (small tensors)",
-                     "kernel_ms_avg": kernel_ms,
+                     "kernel_ms_avg": kernel_ms, "kernel_ms_median": kernel_ms_median,
                      "timing": "HIP events on the launch stream around each step call: all "
-                               "kernels of one step (metadata upload, slot table, step)"},
+                               "kernels of one step (metadata upload, slot table, step)",
+                     "copy_GBps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
+                     "copy_note": "asr_stream_copy, 2 x 8 GiB, a 1:1 copy built like the step "
+                                  "(same slots, 128-bit accesses, XCD windows, residency cap)"},
     }
 
 
@@ -195,6 +206,26 @@ def run_convert(args, torch, ops, wl):
 
 
 GEMM_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def stream_copy_gbps(torch, dev, stream, nbytes=8 << 30, reps=10):
+    """Bandwidth of the library's copy kernel (read + write bytes / time)."""
+    from adamw_optimizer_stochastic_amd import _abi
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        _abi.asr_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream.cuda_stream)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record(stream)
+    for _ in range(reps):
+        _abi.asr_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream.cuda_stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def _time_launches(torch, stream, fn, steps):

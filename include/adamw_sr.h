@@ -272,6 +272,16 @@ int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype,
                 uint64_t base_index, void* stream);
 
 /*
+ * Measurement support: copies `bytes` bytes from src to dst with a kernel
+ * built like the AdamW step (one slot of 16 KiB per workgroup, 128-bit loads
+ * and stores, the step's XCD windows and residency cap). The benchmark
+ * quotes the step's bandwidth against this copy's as well as against the
+ * HBM peak. src, dst: device, 16-byte aligned, not overlapping; bytes a
+ * multiple of 16. Errors: ASR_EINVAL, ASR_EALIGN, ASR_EHIP.
+ */
+int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
  * Test support: the binary32 square root and division exactly as the AdamW
  * kernel evaluates them: sqrt_out[i] = sqrt(a[i]), div_out[i] = a[i] / b[i],
  * both correctly rounded (to nearest even, subnormals kept).
@@ -288,7 +298,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 102
+#define ASR_ABI_VERSION 103
 
 #ifdef __cplusplus
 }

@@ -208,3 +208,13 @@ def test_random_argument_errors():
     assert _status(nrm, 0, E.ASR_BF16, 0, 0.0, 1.0, 1, 2, 0, None) == E.ASR_OK
     assert _status(d, 0, 0, None, E.ASR_BF16, 0, 0.5, 1, 2, 0, None) == E.ASR_OK
     assert _abi.asr_last_error() == ""
+
+
+def test_stream_copy_argument_errors():
+    E = _abi
+    f = _abi.asr_stream_copy
+    assert _status(f, 0x1000, 0x2000, -16, None) == E.ASR_EINVAL
+    assert _status(f, 0, 0x2000, 16, None) == E.ASR_EINVAL
+    assert _status(f, 0x1000, 0x2000, 24, None) == E.ASR_EALIGN
+    assert _status(f, 0x1008, 0x2000, 16, None) == E.ASR_EALIGN
+    assert _status(f, 0, 0, 0, None) == E.ASR_OK

@@ -151,3 +151,19 @@ def test_sqrt_exhaustive_nonnegative():
         s, _ = ops.f32_sqrt_div(a, ones)
         host = np.arange(start, start + step, dtype=np.uint32).view(np.float32)
         assert_f32_equal_or_both_nan(to_host(s), np.sqrt(host), f"sqrt slice {start:#x}")
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1023, 16 * 16384 + 48, (1 << 28) + 16 * 7])
+def test_stream_copy_is_exact(nbytes):
+    """The measurement copy (asr_stream_copy) moves every byte, and no more."""
+    announce("stream copy", nbytes)
+    from adamw_optimizer_stochastic_amd import _abi
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=g)
+    dst = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device=dev)
+    _abi.asr_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes,
+                         torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())
