@@ -69,11 +69,16 @@ class AdamWSR(torch.optim.Optimizer):
         return self._base_index[p]
 
     def _workspace(self, device, numels):
+        """A cached workspace for this device and its current stream. The step
+        kernels read their metadata from the workspace asynchronously, so a
+        workspace is only reused on the stream that last used it (stream
+        order then separates the steps); another stream gets its own."""
         need = ops.workspace_bytes(numels)
-        ws = self._workspaces.get(device)
+        key = (device, torch.cuda.current_stream(device).cuda_stream)
+        ws = self._workspaces.get(key)
         if ws is None or ws.numel() < need:
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-            self._workspaces[device] = ws
+            self._workspaces[key] = ws
         return ws
 
     @torch.no_grad()

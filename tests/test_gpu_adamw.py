@@ -349,6 +349,34 @@ def test_optimizer_param_groups_dtypes_and_roundings():
         assert int(st["step"].item()) == steps[k]
 
 
+def test_optimizer_on_alternating_streams():
+    """Steps issued on two streams in turn (each waiting for the other) match
+    the same steps on one stream: each stream gets its own cached workspace."""
+    announce("AdamWSR two streams")
+    torch.manual_seed(3)
+    w0 = torch.randn(50000, device="cuda").to(torch.bfloat16)
+    a = torch.nn.Parameter(w0.clone())
+    b = torch.nn.Parameter(w0.clone())
+    oa = AdamWSR([a], lr=1e-3, seed=2)
+    ob = AdamWSR([b], lr=1e-3, seed=2)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    grads = [torch.randn(50000, device="cuda").to(torch.bfloat16) for _ in range(4)]
+    torch.cuda.synchronize()
+    for k, g in enumerate(grads):
+        a.grad = g
+        oa.step()
+        b.grad = g
+        stream = side if k % 2 else main
+        stream.wait_stream(main if k % 2 else side)
+        with torch.cuda.stream(stream):
+            ob.step()
+        (main if k % 2 else side).wait_stream(stream)
+    torch.cuda.synchronize()
+    assert len(ob._workspaces) == 2
+    assert torch.equal(a.detach().view(torch.int16), b.detach().view(torch.int16))
+
+
 def test_optimizer_rejects_unsupported_options():
     with pytest.raises(NotImplementedError):
         AdamWSR([torch.zeros(4, device="cuda", requires_grad=True)], amsgrad=True)
