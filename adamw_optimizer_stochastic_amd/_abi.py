@@ -16,7 +16,7 @@ from ._build import LIB_PATH
 ASR_OK, ASR_EINVAL, ASR_EDTYPE, ASR_EALIGN, ASR_EWORKSPACE, ASR_EHIP = range(6)
 ASR_F32, ASR_BF16 = 0, 1
 ASR_ROUND_SR, ASR_ROUND_RN = 0, 1
-ABI_VERSION = 103
+ABI_VERSION = 104
 
 STATUS_NAMES = {ASR_OK: "ASR_OK", ASR_EINVAL: "ASR_EINVAL", ASR_EDTYPE: "ASR_EDTYPE",
                 ASR_EALIGN: "ASR_EALIGN", ASR_EWORKSPACE: "ASR_EWORKSPACE",
@@ -67,6 +67,7 @@ _SIGNATURES = {
     "asr_dropout": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int64,
                                _c.c_double, _c.c_uint32, _c.c_uint32, _c.c_uint64,
                                _c.c_void_p]),
+    "asr_box_muller_given_words": (_c.c_int, [_c.c_void_p] * 4 + [_c.c_int64, _c.c_void_p]),
     "asr_stream_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "asr_gemm_bf16": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                  _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
@@ -182,6 +183,11 @@ def asr_random_normal(out, dtype, n, mean, std, seed, step, base_index, stream):
 def asr_dropout(x, y, mask, dtype, n, p, seed, step, base_index, stream):
     _check(lib().asr_dropout(x, y, mask, dtype, n, p, seed, step, base_index, stream),
            "asr_dropout")
+
+
+def asr_box_muller_given_words(w_even, w_odd, zc, zs, n, stream):
+    _check(lib().asr_box_muller_given_words(w_even, w_odd, zc, zs, n, stream),
+           "asr_box_muller_given_words")
 
 
 def asr_stream_copy(dst, src, nbytes, stream):

@@ -17,7 +17,7 @@
 //   normal   Box-Muller on the pair (2q, 2q+1), which shares a call:
 //            u1 = ((W(2q) >> 8) + 1) * 2**-24, u2 = (W(2q+1) >> 8) * 2**-24,
 //            r = sqrt(-2 ln u1), z(2q) = r cos(2 pi u2), z(2q+1) = r sin(2 pi u2);
-//            y = mean + std * z
+//            y = mean + std * z (log, sin, cos on the hardware units)
 //   dropout  dropped when W < floor(p * 2**32); y = x * (kept ? f32(1/(1-p)) : 0)
 // Every kernel handles 4 consecutive positions per lane: one Philox call
 // when they start on a group of four, two otherwise. All arithmetic is
@@ -88,16 +88,30 @@ __device__ __forceinline__ float unit(uint32_t w) {
   return static_cast<float>(w >> 8) * kTwoM24;  // exact: 24-bit integer times 2**-24
 }
 
-// Standard normal pair of the words (W(2q), W(2q+1)).
+// Standard normal pair of the words (W(2q), W(2q+1)), on the hardware
+// transcendental units: v_log_f32 is log2, and v_sin_f32 / v_cos_f32 take
+// their argument in revolutions, so sin(2 pi u2) is v_sin_f32(u2) with no
+// argument reduction. Each of them only ever sees the 2**24 values
+// (k + 1) * 2**-24 (u1) or k * 2**-24 (u2); the test suite measures their
+// error over all of those inputs through asr_box_muller_given_words, which
+// runs this function.
+constexpr float kTwoLn2 = 1.38629436111989061883f;  // 2 ln 2, rounded to binary32
 __device__ __forceinline__ void box_muller(uint32_t w_even, uint32_t w_odd, float& zc,
                                            float& zs) {
   const float u1 = static_cast<float>((w_even >> 8) + 1u) * kTwoM24;  // (0, 1], exact
   const float u2 = unit(w_odd);
-  const float r = __builtin_sqrtf(-2.0f * logf(u1));
-  float s, c;
-  sincospif(2.0f * u2, &s, &c);  // sin and cos of pi * (2 u2) = 2 pi u2
-  zc = r * c;
-  zs = r * s;
+  // log2 u1 <= 0; its magnitude keeps r = +0 at u1 = 1
+  const float r = __builtin_sqrtf(kTwoLn2 * __builtin_fabsf(__builtin_amdgcn_logf(u1)));
+  zc = r * __builtin_amdgcn_cosf(u2);
+  zs = r * __builtin_amdgcn_sinf(u2);
+}
+
+__global__ void __launch_bounds__(kBlock)
+box_muller_given_words(const uint32_t* __restrict__ w_even, const uint32_t* __restrict__ w_odd,
+                       float* __restrict__ zc, float* __restrict__ zs, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride)
+    box_muller(w_even[i], w_odd[i], zc[i], zs[i]);
 }
 
 template <typename T>
@@ -283,6 +297,23 @@ int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype, int64_t n,
   P.step = step;
   P.vec_ok = aligned_to(x, vec_alignment(dtype)) && aligned_to(y, vec_alignment(dtype));
   return dispatch<asr_rng::kDropout>(P, dtype, static_cast<hipStream_t>(stream), "dropout launch");
+}
+
+int asr_box_muller_given_words(const uint32_t* w_even, const uint32_t* w_odd, float* zc,
+                               float* zs, int64_t n, void* stream) {
+  if (n < 0) return fail(ASR_EINVAL, "n < 0");
+  if (n == 0) return ok();
+  if (!w_even || !w_odd || !zc || !zs) return fail(ASR_EINVAL, "NULL buffer");
+  if (!aligned_to(w_even, 4) || !aligned_to(w_odd, 4) || !aligned_to(zc, 4) || !aligned_to(zs, 4))
+    return fail(ASR_EALIGN, "buffers must be 4-byte aligned");
+  const int64_t blocks = (n + asr_rng::kBlock - 1) / asr_rng::kBlock;
+  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(blocks, 1 << 16));
+  void* argv[] = {&w_even, &w_odd, &zc, &zs, &n};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&asr_rng::box_muller_given_words),
+                                       dim3(grid), dim3(asr_rng::kBlock), argv, 0,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "box-muller launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -246,9 +246,11 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b,
  * asr_random_normal: Box-Muller on position pairs (2q, 2q + 1):
  *   u1 = ((W(2q) >> 8) + 1) * 2**-24, u2 = (W(2q + 1) >> 8) * 2**-24,
  *   r = sqrt(-2 ln u1); z(2q) = r cos(2 pi u2), z(2q + 1) = r sin(2 pi u2);
- *   out[i] = f32(mean) + f32(std) * z. log, sin and cos are the device
- *   library's binary32 functions (a few ulp), so values are reproducible on
- *   this library but not bit-identical to other implementations.
+ *   out[i] = f32(mean) + f32(std) * z. ln is 2 ln 2 * |log2|, and log2,
+ *   sin and cos are gfx950's transcendental instructions (v_log_f32,
+ *   v_sin_f32, v_cos_f32), whose error over every input they can receive
+ *   here is measured by asr_box_muller_given_words; values are reproducible
+ *   on this library but not bit-identical to other implementations.
  *   mean finite, std finite and >= 0.
  * asr_dropout: drop probability p in [0, 1). Element i is dropped when
  *   W < floor(p * 2**32); y[i] = x[i] * (dropped ? 0 : f32(1 / (1 - p))), one
@@ -282,6 +284,16 @@ int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype,
 int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
 /*
+ * Test support: the Box-Muller pair of asr_random_normal from given words:
+ * zc[i], zs[i] = r cos(2 pi u2), r sin(2 pi u2) with u1, u2 from
+ * w_even[i], w_odd[i] as above -- the same device function, so its error
+ * can be measured over every possible input. All buffers: device, n
+ * 4-byte elements. Errors: ASR_EINVAL, ASR_EALIGN, ASR_EHIP.
+ */
+int asr_box_muller_given_words(const uint32_t* w_even, const uint32_t* w_odd,
+                               float* zc, float* zs, int64_t n, void* stream);
+
+/*
  * Test support: the binary32 square root and division exactly as the AdamW
  * kernel evaluates them: sqrt_out[i] = sqrt(a[i]), div_out[i] = a[i] / b[i],
  * both correctly rounded (to nearest even, subnormals kept).
@@ -298,7 +310,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 103
+#define ASR_ABI_VERSION 104
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ is a reading (listed with the others in the design notes):
     u2 = (W(2q + 1) >> 8) * 2**-24, r = sqrt(-2 ln u1); position 2q gets
     r cos(2 pi u2) and 2q + 1 gets r sin(2 pi u2). A draw with mean mu and
     standard deviation s is mu + s * z. The oracle evaluates z in binary64;
-    the device evaluates it in binary32 with library log and sincos, so the
+    the device evaluates it in binary32 on its log2/sin/cos units, so the
     two are compared within a bound.
   * Dropout with drop probability p in [0, 1): threshold T = floor(p * 2**32)
     (binary64), an element is dropped when W < T (so P(drop) = T / 2**32);

@@ -3,12 +3,13 @@ asr_dropout) and the to() conversion surface, against the oracle.
 
 Uniform draws and dropout are integer decisions and exact binary32
 operations on the stream words: bit-exact. Normal draws go through the
-device library's log and sincos: compared with the oracle's binary64 value
-within 2**-20 * (std * r + |mean| + |y|), r the pair's radius. That covers
-a radius error of about 2**-22 relative (log within 2 ulp, a correctly
-rounded sqrt), sincos within 2 ulp, and the rounding of the final multiply
-and add, with a factor-of-two margin. The bf16 form must be the
-round-to-nearest of the kernel's own f32 value.
+hardware log2, sin and cos units: test_box_muller_exhaustive measures, over
+every input those units can receive here (2**24 values of u1, 2**24 of u2),
+a radius error below 2**-22 relative and a sin/cos error below 2**-22
+absolute. So |z - z_exact| <= r * (2**-22 + 2**-22 + 2**-44) + 2**-24 |z|.
+After the final binary32 multiply and add, the normal draws are compared
+within 2**-20 * (std * r + |mean| + |y|), about 2x that. The bf16 form must
+be the round-to-nearest of the kernel's own f32 value.
 Sizes cover one element, ragged tails, several workgroups and unaligned
 starting positions (a pair split across pieces for the normal draws).
 """
@@ -79,6 +80,46 @@ def test_normal_within_bound(n, base):
         gotb = to_host(arng.normal(n, mean, std, seed=seed, step=step, base_index=base,
                                    dtype=torch.bfloat16))
         assert_bits_equal(gotb, oracle.rn_bf16(oracle.f32_bits(got)), "normal bf16 = rn(f32)")
+
+
+E_RADIUS = 2.0 ** -22   # relative error of r = sqrt(-2 ln u1)
+E_TRIG = 2.0 ** -22     # absolute error of cos(2 pi u2), sin(2 pi u2), incl. the product's rounding
+
+
+def test_box_muller_exhaustive():
+    """The Box-Muller pair (asr_box_muller_given_words, the device function
+    the normal kernel runs) over every u1 (with u2 = 0) and every u2 (with
+    u1 = 2**-24, the largest radius) against binary64."""
+    announce("box-muller exhaustive")
+    from adamw_optimizer_stochastic_amd import _abi
+    dev = torch.device("cuda", 0)
+    n = 1 << 24
+    words = (torch.arange(n, dtype=torch.int64, device=dev) << 8).to(torch.int32)  # top 24 bits = k
+    zeros = torch.zeros(n, dtype=torch.int32, device=dev)
+    zc = torch.empty(n, dtype=torch.float32, device=dev)
+    zs = torch.empty(n, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    k = np.arange(n, dtype=np.float64)
+    # every u1 = (k + 1) * 2**-24, u2 = 0: zc = r, zs = 0
+    _abi.asr_box_muller_given_words(words.data_ptr(), zeros.data_ptr(), zc.data_ptr(),
+                                    zs.data_ptr(), n, st)
+    torch.cuda.synchronize()
+    r_dev = to_host(zc).astype(np.float64)
+    assert np.all(to_host(zs) == 0)
+    r64 = np.sqrt(-2.0 * np.log((k + 1) * 2.0 ** -24))
+    assert r_dev[-1] == 0.0 and np.signbit(np.float32(r_dev[-1])) == False  # u1 = 1: r = +0
+    e_r = np.max(np.abs(r_dev[:-1] - r64[:-1]) / r64[:-1])
+    # every u2 = k * 2**-24 at u1 = 2**-24
+    _abi.asr_box_muller_given_words(zeros.data_ptr(), words.data_ptr(), zc.data_ptr(),
+                                    zs.data_ptr(), n, st)
+    torch.cuda.synchronize()
+    rd = r_dev[0]
+    theta = 2.0 * np.pi * k * 2.0 ** -24
+    e_t = max(np.max(np.abs(to_host(zc).astype(np.float64) / rd - np.cos(theta))),
+              np.max(np.abs(to_host(zs).astype(np.float64) / rd - np.sin(theta))))
+    announce(f"radius error 2**{np.log2(e_r):.2f} relative, sin/cos error 2**{np.log2(e_t):.2f}")
+    assert e_r <= E_RADIUS
+    assert e_t <= E_TRIG
 
 
 def test_normal_pieces_and_statistics():
