@@ -24,14 +24,21 @@
 //     instruction's row side, A rows its column side): each lane then ends
 //     up holding runs of 4 consecutive output columns of one row, which is
 //     exactly one Philox call's 4 words and one 8-byte bf16 store.
-//   * Workgroup tile BM x BN, K in stages of 64 (128 bytes per row), two
-//     stages in LDS. Global -> LDS by the gfx950 16-byte LDS-direct load
+//   * Workgroup tile BM x BN (256 x 256, 8 waves of 128 x 64, two per SIMD),
+//     K in tiles of BK = 32 through a ring of STAGES = 4 LDS buffers (128 KiB).
+//     Global -> LDS by the gfx950 16-byte LDS-direct load
 //     (global_load_lds_dwordx4): no VGPR staging. Each wave-wide load fills
-//     1 KiB = 8 rows; the 16-byte chunks of a row are XOR-swizzled so that
-//     the fragment reads (ds_read_b128, 32 rows per instruction) are free of
-//     bank conflicts.
-//   * Rows past M or N and chunks past K load from a 16-byte zero block, so
-//     ragged edges need no masking in the main loop.
+//     1 KiB; the 16-byte chunks of a row are XOR-swizzled so that the
+//     fragment reads (ds_read_b128, 32 rows per instruction) are free of
+//     bank conflicts. The ring waits with vmcnt for exactly the tile it
+//     needs, and its barrier carries no release fence.
+//   * Copy addresses are a scalar tile base plus 32-bit lane offsets. Rows
+//     past M or N are clamped to the last row (their products only reach
+//     outputs that are not stored); chunks past K come from a 16-byte zero
+//     block, so ragged edges need no masking in the MFMA loop.
+//   * Copies and next-step fragment reads are threaded between the MFMAs
+//     (sched_group_barrier), and the tile's barrier sits inside its last
+//     MFMA step so the next tile's first fragments load under MFMAs.
 //   * Tiles are handed to XCDs in contiguous ranges (workgroup b runs on XCD
 //     b % 8) and grouped along M inside each range, so the workgroups that
 //     share an L2 also share A and B panels.
