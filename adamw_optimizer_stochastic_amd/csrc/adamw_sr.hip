@@ -15,11 +15,15 @@
 //
 // Design for the hardware: the step is a pure stream (22 bytes per bf16
 // element, each byte read or written once), so the kernels are built around
-// HBM bandwidth: 128-bit loads and stores of 8 elements per lane, Philox in
-// registers with one call per 4 consecutive positions (no generator state in
-// memory), no LDS and no matrix cores. A multi-tensor chunk table lets one
-// launch cover thousands of tensors: every workgroup takes whole chunks of
-// one tensor and finds its tensor by a wave-uniform binary search.
+// HBM bandwidth: vector loads and stores of 4 elements per lane (128-bit for
+// f32, 64-bit for bf16), Philox in registers with one call per 4 consecutive
+// positions (no generator state in memory), no LDS and no matrix cores.
+// Every workgroup takes one slot of 1,024 elements and exits (no loop); the
+// slots of a launch are spread over eight address windows, one per XCD, and
+// a residency cap (LDS reservation) keeps about 24 KiB in flight per CU.
+// Tensors of equal size share a launch and find their tensor by a
+// multiply-high division of the slot index; the rest use a slot-to-tensor
+// table filled on the device, so one call covers thousands of tensors.
 #include "device.hpp"
 #include "status.hpp"
 
