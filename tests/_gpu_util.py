@@ -70,3 +70,24 @@ def assert_f32_equal_or_both_nan(got, want, what=""):
 def bf16_is_nan(h):
     h = np.asarray(h, dtype=np.uint16)
     return ((h & 0x7F80) == 0x7F80) & ((h & 0x7F) != 0)
+
+
+# Format conversions for checking properties of kernel outputs in the tests
+# (plain bit manipulation; kernel outputs never go through the oracle).
+def bf16_bits_value(h):
+    """bf16 patterns -> float64 values (exact)."""
+    return (np.asarray(h, dtype=np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f32_bits_of(x):
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def within_bf16_step(h_bits, exact, bound):
+    """True where the bf16 value lies within `bound` plus one bf16 ulp (at
+    the larger of |exact| + bound) of `exact` -- what any rounding, SR or
+    RN, of a value within `bound` of `exact` satisfies."""
+    y = bf16_bits_value(h_bits)
+    mag = np.abs(exact) + bound
+    ulp = np.exp2(np.floor(np.log2(np.maximum(mag, 2.0 ** -126))) - 7)
+    return np.abs(y - exact) <= bound + ulp

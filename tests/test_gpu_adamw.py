@@ -16,7 +16,8 @@ from oracle.adamw import F32, BF16, ROUND_SR, ROUND_RN
 from adamw_optimizer_stochastic_amd import ops, AdamWSR
 from adamw_optimizer_stochastic_amd import workloads as wl
 from _gpu_util import (gpu, require_gpu, announce, f32_tensor, bf16_tensor, to_host,
-                       assert_bits_equal, assert_f32_equal_or_both_nan, bf16_is_nan)
+                       assert_bits_equal, assert_f32_equal_or_both_nan, bf16_is_nan,
+                       bf16_bits_value)
 
 pytestmark = gpu
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
@@ -232,7 +233,7 @@ def test_subulp_accumulation_full_size():
     sr = run("sr", 0)
     announce("subulp sr repeat")
     assert np.array_equal(sr, run("sr", 0))
-    mean = oracle.bf16_to_f32(sr).astype(np.float64).mean()
+    mean = bf16_bits_value(sr).mean()
     assert 1.40 < mean < 1.5, mean
 
     hw = np.full(win, 0x3F80, np.uint16)

@@ -79,7 +79,8 @@ def test_normal_within_bound(n, base):
         assert np.all(err <= bound), f"max err/bound {np.max(err / bound)}"
         gotb = to_host(arng.normal(n, mean, std, seed=seed, step=step, base_index=base,
                                    dtype=torch.bfloat16))
-        assert_bits_equal(gotb, oracle.rn_bf16(oracle.f32_bits(got)), "normal bf16 = rn(f32)")
+        assert_bits_equal(gotb, to_host(ops.cvt_f32_bf16_rn(f32_tensor(got))),
+                          "normal bf16 = rn(f32)")
 
 
 E_RADIUS = 2.0 ** -22   # relative error of r = sqrt(-2 ln u1)
