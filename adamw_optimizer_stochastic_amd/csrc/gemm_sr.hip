@@ -25,17 +25,20 @@
 //     up holding runs of 4 consecutive output columns of one row, which is
 //     exactly one Philox call's 4 words and one 8-byte bf16 store.
 //   * Workgroup tile BM x BN (256 x 256, 8 waves of 128 x 64, two per SIMD),
-//     K in tiles of BK = 32 through a ring of STAGES = 4 LDS buffers (128 KiB).
-//     Global -> LDS by the gfx950 16-byte LDS-direct load
-//     (global_load_lds_dwordx4): no VGPR staging. Each wave-wide load fills
-//     1 KiB; the 16-byte chunks of a row are XOR-swizzled so that the
-//     fragment reads (ds_read_b128, 32 rows per instruction) are free of
-//     bank conflicts. The ring waits with vmcnt for exactly the tile it
-//     needs, and its barrier carries no release fence.
-//   * Copy addresses are a scalar tile base plus 32-bit lane offsets. Rows
-//     past M or N are clamped to the last row (their products only reach
-//     outputs that are not stored); chunks past K come from a 16-byte zero
-//     block, so ragged edges need no masking in the MFMA loop.
+//     K in tiles of BK = 64 (one 128-byte cache line per row) through a ring
+//     of STAGES = 2 LDS buffers (128 KiB). Global -> LDS by gfx950's 16-byte
+//     buffer loads to LDS (buffer_load_dwordx4 ... lds): no VGPR staging.
+//     Each wave-wide load fills 1 KiB; the 16-byte chunks of a row are
+//     XOR-swizzled so that the fragment reads (ds_read_b128, 32 rows per
+//     instruction) are free of bank conflicts. All copies of a K tile are
+//     issued at the start of the one before it, the ring waits with vmcnt
+//     for exactly the tile it needs, and its barrier carries no release
+//     fence.
+//   * Copy sources are a buffer resource at the tile origin and K offset
+//     (scalar) plus 32-bit lane offsets. Rows past M or N are clamped to the
+//     last row (their products only reach outputs that are not stored);
+//     chunks past K take an out-of-range offset, for which the buffer load
+//     returns zeros, so ragged edges need no masking in the MFMA loop.
 //   * Copies and next-step fragment reads are threaded between the MFMAs
 //     (sched_group_barrier), and the tile's barrier sits inside its last
 //     MFMA step so the next tile's first fragments load under MFMAs.
@@ -70,8 +73,20 @@ constexpr int kDmaBytes = 1024;    // LDS bytes one wave-wide 16-byte-per-lane D
 #endif
 constexpr bool kSchedule = ASR_GEMM_SCHEDULE;  // see schedule_step
 
-// Source of chunks outside the matrices (rows past M or N, columns past K).
-__device__ __align__(16) uint4 g_zero_chunk;
+// Copies go through buffer resources: a resource spans kBufferRecords bytes
+// from a tile's first row at one K tile, and a lane offset at or past that
+// reads zeros (a buffer load's out-of-range result) without touching memory.
+// Valid offsets stay below it: a tile's rows are at most 255 leading
+// dimensions (< 2**22 elements, so < 2**23 bytes) past its first row.
+constexpr uint32_t kBufferRecords = 0x80000000u;
+constexpr uint32_t kOutOfRange = kBufferRecords;
+constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const char* base) {
+  // (the builtin takes a non-const pointer; the resource is only read)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), static_cast<short>(0),
+                                           static_cast<int32_t>(kBufferRecords), kBufferWord3);
+}
 
 // Workgroup tile BM x BN, wave tile WM x WN, K in stages of BK (32 or 64),
 // STAGES stages in LDS.
@@ -278,9 +293,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   // is rows slab * kSlabRows .. + kSlabRows - 1 of the stage (slab = wave +
   // j * kWaves; the first kSlabsA slabs of every wave lie in A, the rest in
   // B); the lane copies the 16-byte chunk at position lane % kChunks of row
-  // lane / kChunks. Its source is a scalar base (tile origin + K offset)
-  // plus a 32-bit per-lane byte offset. Rows past the edge of A or B are
-  // clamped to the last row: they only feed outputs that are not stored.
+  // lane / kChunks. Its source is a buffer resource at the tile origin and
+  // K offset (scalar) plus a 32-bit per-lane byte offset. Rows past the edge
+  // of A or B are clamped to the last row: they only feed outputs that are
+  // not stored.
   constexpr int kChunks = Cfg::kChunks;
   constexpr int kSlabsA = BM / Cfg::kSlabRows / Cfg::kWaves;
   static_assert((BM / Cfg::kSlabRows) % Cfg::kWaves == 0, "A slabs split evenly over waves");
@@ -301,29 +317,25 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   const char* a_tile = reinterpret_cast<const char*>(args.a + m0 * args.lda);
   const char* b_tile = reinterpret_cast<const char*>(args.b + n0 * args.ldb);
 
-  // Copy of slab j of K tile kt into LDS buffer `stage` (whole tile in K).
-  auto dma = [&](int stage, int j, int kt) {
+  // Copy of slab j of K tile kt into LDS buffer `stage`: a buffer load to
+  // LDS (buffer_load_dwordx4 ... lds) from a resource at the tile's first
+  // row and K tile, with the lane's 32-bit offset. Lanes whose offset is
+  // kOutOfRange write zeros.
+  auto dma_off = [&](int stage, int j, int kt, uint32_t off) {
     const char* base = (j < kSlabsA ? a_tile : b_tile) + static_cast<int64_t>(kt) * Cfg::kRowBytes;
-    // (the builtin takes a non-const global pointer; it only reads it)
-    __builtin_amdgcn_global_load_lds(
-        const_cast<char*>(base + voff[j]),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        buffer_of(base),
         (lds_void_ptr)(smem + stage * Cfg::kStageBytes + (wave + j * Cfg::kWaves) * kDmaBytes),
-        16, 0, 0);
+        16, off, 0, 0, 0);
   };
-  // The same for the last K tile when K is not a multiple of BK: chunks at
-  // or past K come from the zero block (K is a multiple of 8, so a chunk is
-  // wholly inside or wholly outside).
-  const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero_chunk);
+  auto dma = [&](int stage, int j, int kt) { dma_off(stage, j, kt, voff[j]); };
+  // The last K tile when K is not a multiple of BK: chunks at or past K read
+  // zeros (K is a multiple of 8, so a chunk is wholly inside or outside).
   auto dma_tail = [&](int stage, int j, int kt) {
     const uint32_t row = (wave + j * Cfg::kWaves) * Cfg::kSlabRows + lane / kChunks;
     const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);
     const int k = kt * Cfg::BK + static_cast<int>(c) * 8;
-    const char* base = (j < kSlabsA ? a_tile : b_tile) + static_cast<int64_t>(kt) * Cfg::kRowBytes;
-    const void* g = k < args.k ? static_cast<const void*>(base + voff[j])
-                               : static_cast<const void*>(zero);
-    __builtin_amdgcn_global_load_lds(
-        const_cast<void*>(g), (lds_void_ptr)(smem + stage * Cfg::kStageBytes + (wave + j * Cfg::kWaves) * kDmaBytes),
-        16, 0, 0);
+    dma_off(stage, j, kt, k < args.k ? voff[j] : kOutOfRange);
   };
 
   f32x16 acc[Cfg::kFragM][Cfg::kFragN];
@@ -337,12 +349,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   const int ktiles = (args.k + Cfg::BK - 1) / Cfg::BK;
   const int kfull = args.k / Cfg::BK;  // K tiles with no chunk past K
   constexpr int kSteps = Cfg::BK / 16;  // MFMA steps per K tile
-  constexpr int kDmaPerStep = (Cfg::kSlabsPerWave + kSteps - 1) / kSteps;
 
-  // Ring of STAGES buffers: tile kt lives in buffer kt % STAGES, and the
-  // copies of tile kt + STAGES - 1 are issued while tile kt is multiplied,
-  // spread over its MFMA steps. Fragments are read one step ahead, the
-  // first step's across the tile boundary (see tile_body).
+  // Ring of STAGES buffers: tile kt lives in buffer kt % STAGES, and all
+  // copies of tile kt + STAGES - 1 are issued at the start of tile kt (its
+  // buffer last held tile kt - 1, which every wave finished reading before
+  // the barrier inside tile kt - 1), so they have a whole tile to land.
+  // Fragments are read one step ahead, the first step's across the tile
+  // boundary (see tile_body).
   int cur = 0;                     // buffer of tile kt
   int fill = Cfg::STAGES - 1;      // buffer of tile kt + STAGES - 1
   bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
@@ -383,10 +396,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
     static_for<kSteps>([&](auto kkc) {
       constexpr int kk = decltype(kkc)::value;
       if constexpr (kk + 1 < kSteps) read_frags_from(sa, kk + 1, (kk + 1) & 1);
-      if constexpr (LOAD == 1) {
+      if constexpr (LOAD == 1 && kk == 0) {
 #pragma unroll
-        for (int d = 0; d < kDmaPerStep; ++d)
-          if (kk * kDmaPerStep + d < Cfg::kSlabsPerWave) dma(fill, kk * kDmaPerStep + d, next);
+        for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma(fill, j, next);
       }
       constexpr int kHalf = kk + 1 < kSteps ? Cfg::kFragM : Cfg::kFragM / 2;
 #pragma unroll
@@ -396,7 +408,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
                                                                acc[i][j], 0, 0, 0);
       if constexpr (kk + 1 < kSteps) {
-        if constexpr (kSchedule) schedule_step<Cfg, kk, kSteps, LOAD == 1 ? kDmaPerStep : 0>();
+        constexpr int kDmas = LOAD == 1 && kk == 0 ? Cfg::kSlabsPerWave : 0;
+        if constexpr (kSchedule) schedule_step<Cfg, kk, kSteps, kDmas>();
       } else {
         __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < ktiles) {
@@ -427,10 +440,6 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
       for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(s, j, s);
     }
   }
-  // Three phases, each a loop over one instance of the body (an if/else of
-  // two instances inside one loop costs registers): copies of whole tiles;
-  // the copy of the partial last tile, if K has one and it was not already
-  // issued by the prologue; no copies.
   // Three phases, each a loop over one instance of the body (an if/else of
   // two instances inside one loop costs registers): copies of whole tiles;
   // the copy of the partial last tile, if K has one and it was not already
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 }
 
 #ifndef ASR_GEMM_BIG
-#define ASR_GEMM_BIG 256, 256, 128, 64, 32, 4
+#define ASR_GEMM_BIG 256, 256, 128, 64, 64, 2
 #endif
 #ifndef ASR_GEMM_SMALL
 #define ASR_GEMM_SMALL 128, 128, 64, 64, 64, 2
@@ -528,9 +537,9 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb
   if (m == 0 || n == 0) return ok();
   if (!c || (k > 0 && (!a || !b))) return fail(ASR_EINVAL, "gemm: null matrix pointer");
   if (lda < k || ldb < k || ldc < n) return fail(ASR_EINVAL, "gemm: lda, ldb >= k and ldc >= n");
-  // the copies address a tile's rows by 32-bit byte offsets from its first row
-  if (lda >= (int64_t{1} << 23) || ldb >= (int64_t{1} << 23))
-    return fail(ASR_EINVAL, "gemm: lda and ldb must be below 2**23");
+  // the copies address a tile's rows by byte offsets below 2**31 from its first row
+  if (lda >= (int64_t{1} << 22) || ldb >= (int64_t{1} << 22))
+    return fail(ASR_EINVAL, "gemm: lda and ldb must be below 2**22");
   if (k % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0)
     return fail(ASR_EALIGN, "gemm: k, lda and ldb must be multiples of 8");
   if (!aligned_to(a, 16) || !aligned_to(b, 16))

@@ -216,7 +216,7 @@ int asr_sr_bf16_given_bits(const float* x, const uint16_t* r16, uint16_t* out,
  * a device f32 buffer with the same row stride ldc that receives the
  * unrounded f32 result. No output may overlap an input.
  * Requirements: 0 <= M, N, K < 2**31; K, lda, ldb multiples of 8;
- * K <= lda < 2**23, K <= ldb < 2**23, ldc >= N; a and b 16-byte aligned; c and c_f32 aligned to
+ * K <= lda < 2**22, K <= ldb < 2**22, ldc >= N; a and b 16-byte aligned; c and c_f32 aligned to
  * their element size; base_index + M*N <= 2**64. M or N = 0 writes
  * nothing; K = 0 writes zeros.
  * Errors: ASR_EINVAL (sizes, strides, rounding, NULL), ASR_EALIGN,

@@ -172,7 +172,8 @@ def test_gemm_argument_errors():
     assert g(ldc=31) == E.ASR_EINVAL          # ldc < n
     assert g(k=60, lda=64, ldb=64) == E.ASR_EALIGN   # k not a multiple of 8
     assert g(lda=68) == E.ASR_EALIGN
-    assert g(lda=2**23) == E.ASR_EINVAL
+    assert g(lda=2**22) == E.ASR_EINVAL      # tile offsets must stay below 2**31
+    assert g(ldb=2**22) == E.ASR_EINVAL
     assert g(a=0x1008) == E.ASR_EALIGN        # A not 16-byte aligned
     assert g(c=0x3001) == E.ASR_EALIGN
     assert g(c32=0x4002) == E.ASR_EALIGN
