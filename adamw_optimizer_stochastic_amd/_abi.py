@@ -16,7 +16,7 @@ from ._build import LIB_PATH
 ASR_OK, ASR_EINVAL, ASR_EDTYPE, ASR_EALIGN, ASR_EWORKSPACE, ASR_EHIP = range(6)
 ASR_F32, ASR_BF16 = 0, 1
 ASR_ROUND_SR, ASR_ROUND_RN = 0, 1
-ABI_VERSION = 104
+ABI_VERSION = 105
 
 STATUS_NAMES = {ASR_OK: "ASR_OK", ASR_EINVAL: "ASR_EINVAL", ASR_EDTYPE: "ASR_EDTYPE",
                 ASR_EALIGN: "ASR_EALIGN", ASR_EWORKSPACE: "ASR_EWORKSPACE",

@@ -310,7 +310,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 104
+#define ASR_ABI_VERSION 105
 
 #ifdef __cplusplus
 }
