@@ -219,11 +219,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Instruction order of one MFMA step, imposed on the compiler's scheduler
-// (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x020 global
-// read, which includes the LDS-direct copies). The reads of the next step's
-// fragments and this step's copies are threaded between this step's MFMAs,
-// so they are issued early, into registers distinct from the ones the
-// MFMAs read, and the wait for them falls after a run of MFMAs.
+// (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x020 vector
+// memory read, which includes the copies to LDS). This step's copies and
+// the reads of the next step's fragments are threaded between this step's
+// MFMAs, a copy first after each MFMA (the copies then leave as early as
+// possible), so the reads go into registers distinct from the ones the
+// MFMAs read and the wait for them falls after a run of MFMAs.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
 template <typename Cfg, int KK, int STEPS, int DMAS>
 __device__ __forceinline__ void schedule_step() {
@@ -232,14 +233,11 @@ __device__ __forceinline__ void schedule_step() {
   static_for<kMfma>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (i < DMAS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
     if constexpr (i < kReads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    if constexpr (i >= kReads && i - kReads < DMAS)
-      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
   });
+  if constexpr (DMAS > kMfma) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, DMAS - kMfma, 0);
   if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads - kMfma, 0);
-  if constexpr (kReads + DMAS > kMfma)
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead,
-                                         kReads + DMAS - kMfma > DMAS ? DMAS : kReads + DMAS - kMfma, 0);
 }
 
 // Writes output elements (m, n .. n+3) that lie inside C: the f32 values
