@@ -225,3 +225,53 @@ def test_degenerate_sizes():
     with pytest.raises(ops.AsrError):
         ops.gemm_bf16(torch.ones((4, 12), dtype=torch.bfloat16, device=dev),
                       torch.ones((4, 12), dtype=torch.bfloat16, device=dev))  # K % 8 != 0
+
+
+def _sample_grid(extent, tile, count, rng):
+    """Sorted distinct indices in [0, extent): both ends, both sides of the
+    first and the last tile boundary, and `count` random ones."""
+    picks = {0, extent - 1, tile - 1, tile, extent - tile, extent - tile - 1}
+    picks |= set(rng.choice(extent, size=count, replace=False).tolist())
+    return np.array(sorted(p for p in picks if 0 <= p < extent))
+
+
+@pytest.mark.parametrize("kind", ["int", "randn"])
+def test_full_size_llama_mlp_sampled(kind):
+    """The benchmark's workload, 8192 x 14336 x 4096, in its launch
+    configuration (256 x 256 tiles, SR without the f32 copy, seed 7, base 0),
+    checked on a grid of about 72 x 72 sampled outputs. Integer operands make every
+    f32 partial sum exact (|sum| <= 4096 * 64 < 2**24), so the sampled SR and
+    RN outputs must equal the oracle's roundings of the exact products bit for
+    bit; normal operands must lie within a bf16 step of the exact product plus
+    the f32 summation bound."""
+    shape = wl.GEMM_LLAMA3_8B_MLP_UP
+    m, n, k = shape["m"], shape["n"], shape["k"]
+    announce("gemm full size sampled", (m, n, k, kind))
+    a, b = wl.gemm_operands_host(m, n, k, kind, seed=11)
+    rng = np.random.default_rng(5)
+    rows = _sample_grid(m, 256, 66, rng)
+    cols = _sample_grid(n, 256, 66, rng)
+    ad, bd = bf16_tensor(a), bf16_tensor(b)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ri = torch.from_numpy(rows).cuda()
+    ci = torch.from_numpy(cols).cuda()
+    seed, step = 7, 3
+    ops.gemm_bf16(ad, bd, rounding="sr", seed=seed, step=step, out=c)
+    got_sr = to_host(c[ri][:, ci])
+    ops.gemm_bf16(ad, bd, rounding="rn", out=c)
+    got_rn = to_host(c[ri][:, ci])
+    exact = oracle.gemm_exact(a[rows], b[cols])
+    rr, cc = np.meshgrid(rows, cols, indexing="ij")
+    if kind == "int":
+        assert np.all(np.abs(exact) < 2 ** 24)
+        want_sr = oracle.gemm_round_at(exact.astype(np.float32).reshape(-1), rr.reshape(-1),
+                                       cc.reshape(-1), n, seed, step, 0)
+        assert_bits_equal(got_sr.reshape(-1), want_sr, "full-size SR")
+        want_rn = oracle.gemm_round(exact.astype(np.float32), "rn")
+        assert_bits_equal(got_rn.reshape(-1), want_rn.reshape(-1), "full-size RN")
+    else:
+        bound = oracle.f32_sum_bound(a[rows], b[cols])
+        assert within_bf16_step(got_sr, exact, bound).all()
+        assert within_bf16_step(got_rn, exact, bound).all()
+        # SR and RN pick neighbours of the same f32 value: at most one bf16 step apart
+        assert _bf16_steps_apart(got_sr.reshape(-1), got_rn.reshape(-1)).max() <= 1
