@@ -28,6 +28,24 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def check_disjoint(spans):
+    """Raise ValueError if any two of the byte ranges overlap. spans: an
+    iterable of (start, nbytes, name); empty ranges are ignored."""
+    live = sorted((int(a), int(a) + int(n), name) for a, n, name in spans if int(n) > 0)
+    for (a0, e0, n0), (a1, _, n1) in zip(live, live[1:]):
+        if a1 < e0:
+            raise ValueError(f"{n0} and {n1} share memory; every buffer of the step "
+                             "must be disjoint from the others")
+
+
+def _extent(t, name):
+    """(start, nbytes, name) of the memory a strided tensor spans."""
+    if t.numel() == 0:
+        return (t.data_ptr(), 0, name)
+    last = sum((size - 1) * stride for size, stride in zip(t.shape, t.stride()))
+    return (t.data_ptr(), (last + 1) * t.element_size(), name)
+
+
 def workspace_bytes(numels):
     """Workspace bytes for a list of tensors with these element counts."""
     return _abi.asr_adamw_workspace_bytes([dict(numel=int(n)) for n in numels])
@@ -69,6 +87,10 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
         descs.append(_abi.AsrTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
                                     p.numel(), int(b) & 0xFFFFFFFFFFFFFFFF,
                                     _DTYPE_CODE[p.dtype], _DTYPE_CODE[g.dtype]))
+    # p, m and v are written in place, so no buffer may share memory with another
+    check_disjoint((t.data_ptr(), t.numel() * t.element_size(), f"{name}[{i}]")
+                   for i, ts in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs))
+                   for t, name in zip(ts, ("param", "grad", "exp_avg", "exp_avg_sq")))
     need = _abi.asr_adamw_workspace_bytes(descs)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
@@ -106,6 +128,7 @@ def _convert_args(x, out):
     _require_gpu(out, "out")
     if out.dtype != torch.bfloat16 or out.numel() != x.numel() or out.device != x.device:
         raise ValueError("out must be bfloat16 with x's size, on x's device")
+    check_disjoint([_extent(x, "x"), _extent(out, "out")])
     return out
 
 
@@ -161,6 +184,11 @@ def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, ou
                 or out_f32.device != a.device or out_f32.stride() != out.stride():
             raise ValueError("out_f32 must be a float32 (M, N) tensor with out's strides")
         f32_ptr = out_f32.data_ptr()
+    outputs = [_extent(out, "out")] + ([_extent(out_f32, "out_f32")] if out_f32 is not None else [])
+    check_disjoint(outputs)
+    for o in outputs:
+        for i in (_extent(a, "a"), _extent(b, "b")):
+            check_disjoint([o, i])
     # a row stride only matters when there is a second row and a K to walk
     lda = a.stride(0) if m > 1 and k > 0 else max(k, 8)
     ldb = b.stride(0) if n > 1 and k > 0 else max(k, 8)
@@ -224,6 +252,7 @@ def sr_bf16_given_bits(x, r16, *, out=None):
     if x.dtype != torch.float32 or r16.dtype != torch.int16 or r16.numel() != x.numel():
         raise ValueError("x must be float32 and r16 int16 of the same size")
     out = _convert_args(x, out)
+    check_disjoint([_extent(r16, "r16"), _extent(out, "out")])
     with torch.cuda.device(x.device):
         _abi.asr_sr_bf16_given_bits(x.data_ptr(), r16.data_ptr(), out.data_ptr(), x.numel(),
                                     _stream(x.device))

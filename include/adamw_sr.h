@@ -107,7 +107,9 @@ size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors);
  * position base_index + i) or by RN (ASR_ROUND_RN).
  *
  * tensors      host array of n_tensors descriptors (read during the call only);
- *              buffers of different tensors must not overlap.
+ *              the param, grad, exp_avg and exp_avg_sq buffers of all tensors
+ *              must be pairwise disjoint (not checked here; the Python
+ *              binding checks).
  * lr           >= 0, finite.       beta1, beta2   in [0, 1).
  * eps          >= 0, finite.       weight_decay   >= 0, finite.
  * step         1-based step count t, in [1, 2**32 - 1]; used for the bias

@@ -448,3 +448,20 @@ def test_degenerate_hyperparameters(hp):
         _check_outputs((pd, md, vd), want, pdt, f"pdt={pdt}", nan_ok=True)
         if hp["lr"] == 0.0:
             assert_bits_equal(to_host(pd), p, "lr = 0 keeps the parameters")
+
+
+def test_overlapping_buffers_are_rejected():
+    """p, m and v are written in place, so the binding refuses buffers that
+    share memory (here: one tensor's exp_avg_sq is a view into another's
+    exp_avg), before anything is launched."""
+    announce("overlap rejected")
+    n = 1024
+    p = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    g = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    big = torch.zeros(3 * n, dtype=torch.float32, device="cuda")
+    m = [big[:n], torch.zeros(n, dtype=torch.float32, device="cuda")]
+    v = [torch.zeros(n, dtype=torch.float32, device="cuda"), big[n // 2:n // 2 + n]]
+    with pytest.raises(ValueError, match="share memory"):
+        ops.adamw_step(p, g, m, v, [0, n], lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                       weight_decay=0.0, step=1, seed=0)
+    assert float(big.abs().sum()) == 0.0

@@ -275,3 +275,20 @@ def test_full_size_llama_mlp_sampled(kind):
         assert within_bf16_step(got_rn, exact, bound).all()
         # SR and RN pick neighbours of the same f32 value: at most one bf16 step apart
         assert _bf16_steps_apart(got_sr.reshape(-1), got_rn.reshape(-1)).max() <= 1
+
+
+def test_output_sharing_input_memory_is_rejected():
+    """The GEMM's outputs may not share memory with A, B or each other (the
+    binding checks before launching)."""
+    announce("gemm overlap rejected")
+    buf = torch.zeros(64 * 64, dtype=torch.bfloat16, device="cuda")
+    a = buf[:32 * 64].view(32, 64)
+    b = torch.zeros(16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="share memory"):
+        ops.gemm_bf16(a, b, out=buf[16 * 64:16 * 64 + 32 * 16].view(32, 16))
+    raw = torch.zeros(32 * 16 * 4, dtype=torch.uint8, device="cuda")
+    out_f32 = raw.view(torch.float32).view(32, 16)
+    out = raw.view(torch.bfloat16)[:32 * 16].view(32, 16)   # the first half of out_f32's bytes
+    with pytest.raises(ValueError, match="share memory"):
+        ops.gemm_bf16(a, b, out=out, out_f32=out_f32)
+    assert int(raw.sum()) == 0 and int(buf.abs().sum()) == 0

@@ -59,3 +59,15 @@ def test_state_dict_round_trip_keeps_f32_states():
         assert torch.equal(s2["exp_avg"], s["exp_avg"])
         assert torch.equal(s2["exp_avg_sq"], s["exp_avg_sq"])
         assert float(s2["step"]) == 3.0
+
+
+def test_check_disjoint():
+    from adamw_optimizer_stochastic_amd.ops import check_disjoint
+    check_disjoint([(0, 16, "a"), (16, 16, "b"), (64, 0, "empty"), (40, 8, "c")])
+    check_disjoint([(100, 0, "x"), (100, 4, "y")])          # empty ranges never overlap
+    with pytest.raises(ValueError, match="b.*c|c.*b"):
+        check_disjoint([(0, 16, "a"), (32, 16, "b"), (47, 4, "c")])   # one byte shared
+    with pytest.raises(ValueError):
+        check_disjoint([(8, 8, "inner"), (0, 32, "outer")])  # nested
+    with pytest.raises(ValueError):
+        check_disjoint([(0, 8, "p"), (0, 8, "p again")])     # identical
