@@ -39,9 +39,11 @@
 //     last row (their products only reach outputs that are not stored);
 //     chunks past K take an out-of-range offset, for which the buffer load
 //     returns zeros, so ragged edges need no masking in the MFMA loop.
-//   * Copies and next-step fragment reads are threaded between the MFMAs
-//     (sched_group_barrier), and the tile's barrier sits inside its last
-//     MFMA step so the next tile's first fragments load under MFMAs.
+//   * Each MFMA step runs in a fixed order, fenced with sched_barrier so
+//     the compiler keeps it: after every MFMA one copy (first step of a
+//     tile) and one fragment read for the next step. The tile's barrier
+//     sits inside its last MFMA step so the next tile's first fragments
+//     load under MFMAs.
 //   * Tiles are handed to XCDs in contiguous ranges (workgroup b runs on XCD
 //     b % 8) and grouped along M inside each range, so the workgroups that
 //     share an L2 also share A and B panels.
@@ -68,10 +70,6 @@ constexpr int kXcds = 8;
 #endif
 constexpr int kGroupM = ASR_GEMM_GROUP_M;  // tile rows per group in the tile order
 constexpr int kDmaBytes = 1024;    // LDS bytes one wave-wide 16-byte-per-lane DMA fills
-#ifndef ASR_GEMM_SCHEDULE
-#define ASR_GEMM_SCHEDULE 1
-#endif
-constexpr bool kSchedule = ASR_GEMM_SCHEDULE;  // see schedule_step
 
 // Copies go through buffer resources: a resource spans kBufferRecords bytes
 // from a tile's first row at one K tile, and a lane offset at or past that
@@ -218,28 +216,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Instruction order of one MFMA step, imposed on the compiler's scheduler
-// (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x020 vector
-// memory read, which includes the copies to LDS). This step's copies and
-// the reads of the next step's fragments are threaded between this step's
-// MFMAs, a copy first after each MFMA (the copies then leave as early as
-// possible), so the reads go into registers distinct from the ones the
-// MFMAs read and the wait for them falls after a run of MFMAs.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
-template <typename Cfg, int KK, int STEPS, int DMAS>
-__device__ __forceinline__ void schedule_step() {
-  constexpr int kMfma = Cfg::kFragM * Cfg::kFragN;
-  constexpr int kReads = KK + 1 < STEPS ? Cfg::kFragM + Cfg::kFragN : 0;
-  static_for<kMfma>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if constexpr (i < DMAS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-    if constexpr (i < kReads) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-  });
-  if constexpr (DMAS > kMfma) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, DMAS - kMfma, 0);
-  if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads - kMfma, 0);
-}
-
 // Writes output elements (m, n .. n+3) that lie inside C: the f32 values
 // when requested, and their bf16 roundings.
 template <int ROUND, bool F32OUT>
@@ -377,6 +353,24 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
       fb[buf][j] = *reinterpret_cast<const bf16x8*>(
           sb + Cfg::chunk_offset(wn * Cfg::WN + j * 32 + frag_row, c));
   };
+  // Fragment read r of step kk into set buf: A fragment r for r < kFragM,
+  // else B fragment r - kFragM.
+  auto read_frag = [&](const unsigned char* sa, int kk, int buf, auto rc) {
+    constexpr int r = decltype(rc)::value;
+    const uint32_t c = 2 * kk + frag_half;
+    if constexpr (r < Cfg::kFragM)
+      fa[buf][r] = *reinterpret_cast<const bf16x8*>(
+          sa + Cfg::chunk_offset(wm * Cfg::WM + r * 32 + frag_row, c));
+    else
+      fb[buf][r - Cfg::kFragM] = *reinterpret_cast<const bf16x8*>(
+          sa + BM * Cfg::kRowBytes +
+          Cfg::chunk_offset(wn * Cfg::WN + (r - Cfg::kFragM) * 32 + frag_row, c));
+  };
+  auto mfma = [&](int kk, auto ic, auto jc) {
+    constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j],
+                                                         0, 0, 0);
+  };
   auto wait_for = [&](int tile) {  // this lane's copies of tile `tile` have landed
     if (tile + Cfg::STAGES - 2 < ktiles) wait_vmcnt<(Cfg::STAGES - 2) * Cfg::kSlabsPerWave>();
     else wait_vmcnt<0>();
@@ -391,37 +385,56 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
     }
     const unsigned char* sa = smem + cur * Cfg::kStageBytes;
     const unsigned char* na = smem + (cur + 1 == Cfg::STAGES ? 0 : cur + 1) * Cfg::kStageBytes;
+    // Explicit order, fenced so the compiler keeps it: in every step, group
+    // g is MFMA g, then copy g (step 0 of a loading tile), then fragment
+    // read g for the next step. No MFMA moves into another step, so each
+    // accumulator is updated once per step and the reads have a step's
+    // worth of MFMAs to land in.
     static_for<kSteps>([&](auto kkc) {
       constexpr int kk = decltype(kkc)::value;
-      if constexpr (kk + 1 < kSteps) read_frags_from(sa, kk + 1, (kk + 1) & 1);
-      if constexpr (LOAD == 1 && kk == 0) {
-#pragma unroll
-        for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma(fill, j, next);
-      }
-      constexpr int kHalf = kk + 1 < kSteps ? Cfg::kFragM : Cfg::kFragM / 2;
-#pragma unroll
-      for (int i = 0; i < kHalf; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
-                                                               acc[i][j], 0, 0, 0);
-      if constexpr (kk + 1 < kSteps) {
-        constexpr int kDmas = LOAD == 1 && kk == 0 ? Cfg::kSlabsPerWave : 0;
-        if constexpr (kSchedule) schedule_step<Cfg, kk, kSteps, kDmas>();
-      } else {
+      constexpr bool kLast = kk + 1 == kSteps;
+      constexpr int kReads = kLast ? 0 : Cfg::kFragM + Cfg::kFragN;
+      constexpr int kDmas = LOAD == 1 && kk == 0 ? Cfg::kSlabsPerWave : 0;
+      constexpr int kRows = kLast ? Cfg::kFragM / 2 : Cfg::kFragM;
+      constexpr int kMf = kRows * Cfg::kFragN;
+      static_for<kMf>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        mfma(kk, std::integral_constant<int, g / Cfg::kFragN>{},
+             std::integral_constant<int, g % Cfg::kFragN>{});
+        if constexpr (g < kDmas) dma(fill, g, next);
+        if constexpr (g < kReads) read_frag(sa, kk + 1, (kk + 1) & 1, gc);
         __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<(kDmas > kMf ? kDmas - kMf : 0)>([&](auto dc) {
+        dma(fill, kMf + decltype(dc)::value, next);
+      });
+      static_for<(kReads > kMf ? kReads - kMf : 0)>([&](auto rc) {
+        read_frag(sa, kk + 1, (kk + 1) & 1,
+                  std::integral_constant<int, kMf + decltype(rc)::value>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kLast) {
+        // the barrier, then the other half of the MFMAs, each followed by
+        // a read of the next tile's first step (harmless after the last
+        // tile: the LDS is only read, and the values are not used)
         if (kt + 1 < ktiles) {
           wait_for(kt + 1);
           barrier_lds();  // tile kt + 1 visible; every wave is done with tile kt - 1's buffer
-          read_frags_from(na, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = kHalf; i < Cfg::kFragM; ++i)
-#pragma unroll
-          for (int j = 0; j < Cfg::kFragN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
-                                                                 acc[i][j], 0, 0, 0);
+        constexpr int kRest = (Cfg::kFragM - kRows) * Cfg::kFragN;
+        constexpr int kNext = Cfg::kFragM + Cfg::kFragN;
+        static_for<kRest>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          if constexpr (g < kNext) read_frag(na, 0, 0, gc);
+          mfma(kk, std::integral_constant<int, kRows + g / Cfg::kFragN>{},
+               std::integral_constant<int, g % Cfg::kFragN>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for<(kNext > kRest ? kNext - kRest : 0)>([&](auto rc) {
+          read_frag(na, 0, 0, std::integral_constant<int, kRest + decltype(rc)::value>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
       }
     });
     cur = cur + 1 == Cfg::STAGES ? 0 : cur + 1;
