@@ -408,7 +408,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the optimizer step has no cross-GPU exchange "
               "(each rank would run the same kernel on its own shard with its own "
-              "base_index), and this build runs on a single MI355X; use --gpus 1.",
+              "base_index); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
