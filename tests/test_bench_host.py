@@ -1,0 +1,48 @@
+"""Host logic of bench.py (CPU only): the kernel-source hash that keeps the
+committed HBM counters tied to the code they were taken on, and the rule that
+`traffic` is reported only while that hash (and the element count) match."""
+
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _hash_of(tmp_path, monkeypatch, text):
+    f = tmp_path / "k.hip"
+    f.write_text(text)
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(f)])
+    return bench.source_hash()
+
+
+def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
+    code = "int f(int x) {\n  return x + 1;\n}\n"
+    h0 = _hash_of(tmp_path, monkeypatch, code)
+    assert _hash_of(tmp_path, monkeypatch, "// a comment\n" + code) == h0
+    assert _hash_of(tmp_path, monkeypatch, "/* block\n comment */ " + code.replace("  ", "    ")) == h0
+    assert _hash_of(tmp_path, monkeypatch, code.replace("x + 1", "x + 2")) != h0
+
+
+def test_traffic_only_for_matching_code_and_size(tmp_path, monkeypatch):
+    doc = {"source_hash": "abc", "n_elems": 100, "hbm_bytes_per_launch": 2200.0}
+    (tmp_path / "adamw_sr_w_hbm_counters.json").write_text(json.dumps(doc))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    monkeypatch.setattr(bench, "source_hash", lambda: "abc")
+    assert bench.traffic_from_profile("w", 100) == 2200.0
+    assert bench.traffic_from_profile("w", 101) is None        # another workload size
+    assert bench.traffic_from_profile("other", 100) is None    # no counters for it
+    monkeypatch.setattr(bench, "source_hash", lambda: "def")
+    assert bench.traffic_from_profile("w", 100) is None        # kernel code changed
+
+
+def test_committed_counters_describe_the_llama_list():
+    path = os.path.join(ROOT, "profiles", "adamw_sr_llama3_8b_hbm_counters.json")
+    with open(path) as fh:
+        doc = json.load(fh)
+    assert doc["n_elems"] == 8030261248
+    # scaled counter bytes equal the algorithmic 22 B/element to within 0.1%
+    assert abs(doc["hbm_bytes_per_launch"] / (22 * doc["n_elems"]) - 1) < 1e-3
