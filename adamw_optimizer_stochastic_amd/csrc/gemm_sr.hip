@@ -30,20 +30,20 @@
 //     buffer loads to LDS (buffer_load_dwordx4 ... lds): no VGPR staging.
 //     Each wave-wide load fills 1 KiB; the 16-byte chunks of a row are
 //     XOR-swizzled so that the fragment reads (ds_read_b128, 32 rows per
-//     instruction) are free of bank conflicts. All copies of a K tile are
-//     issued at the start of the one before it, the ring waits with vmcnt
-//     for exactly the tile it needs, and its barrier carries no release
-//     fence.
+//     instruction) are free of bank conflicts. A K tile's copies are issued
+//     into the buffer of the tile two before it as soon as every wave has
+//     passed that tile's barrier, the ring waits with vmcnt for exactly the
+//     tile it needs, and its barrier carries no release fence.
 //   * Copy sources are a buffer resource at the tile origin and K offset
 //     (scalar) plus 32-bit lane offsets. Rows past M or N are clamped to the
 //     last row (their products only reach outputs that are not stored);
 //     chunks past K take an out-of-range offset, for which the buffer load
 //     returns zeros, so ragged edges need no masking in the MFMA loop.
 //   * Each MFMA step runs in a fixed order, fenced with sched_barrier so
-//     the compiler keeps it: after every MFMA one copy (first step of a
-//     tile) and one fragment read for the next step. The tile's barrier
-//     sits inside its last MFMA step so the next tile's first fragments
-//     load under MFMAs.
+//     the compiler keeps it: after every MFMA one fragment read for the
+//     next step. The tile's barrier sits inside its last MFMA step, so the
+//     next tile's first fragments and the copies of the tile two ahead
+//     issue under the MFMAs that follow it.
 //   * Tiles are handed to XCDs in contiguous ranges (workgroup b runs on XCD
 //     b % 8) and grouped along M inside each range, so the workgroups that
 //     share an L2 also share A and B panels.
@@ -324,23 +324,23 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   const int kfull = args.k / Cfg::BK;  // K tiles with no chunk past K
   constexpr int kSteps = Cfg::BK / 16;  // MFMA steps per K tile
 
-  // Ring of STAGES buffers: tile kt lives in buffer kt % STAGES, and all
-  // copies of tile kt + STAGES - 1 are issued at the start of tile kt (its
-  // buffer last held tile kt - 1, which every wave finished reading before
-  // the barrier inside tile kt - 1), so they have a whole tile to land.
-  // Fragments are read one step ahead, the first step's across the tile
-  // boundary (see tile_body).
+  // Ring of STAGES buffers: tile kt lives in buffer kt % STAGES. The copies
+  // of tile kt + STAGES go into tile kt's own buffer as soon as every wave
+  // has passed the barrier inside tile kt's last MFMA step (by then all of
+  // tile kt's fragments are in registers), so they have STAGES - 1 tiles
+  // and the rest of that step to land. Fragments are read one step ahead,
+  // the first step's across the tile boundary (see tile_body).
   int cur = 0;                     // buffer of tile kt
-  int fill = Cfg::STAGES - 1;      // buffer of tile kt + STAGES - 1
   bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
 
-  // LOAD: 0 = no copies, 1 = whole tile, 2 = the partial last tile.
+  // LOAD (the copies a tile body issues, of tile kt + STAGES): 0 = none,
+  // 1 = a whole tile, 2 = the partial last tile.
   // The barrier sits inside the last MFMA step of each tile.
   // Half of that step's MFMAs are issued, then the wave waits for tile
-  // kt + 1, passes the barrier and issues tile kt + 1's first fragment
-  // reads, and the other half of the MFMAs cover their latency. The next
-  // tile then starts with its fragments in registers instead of behind a
-  // barrier and a round trip to the LDS.
+  // kt + 1, passes the barrier, and issues tile kt + 1's first fragment
+  // reads and the copies of tile kt + STAGES between the other half of the
+  // MFMAs. The next tile then starts with its fragments in registers
+  // instead of behind a barrier and a round trip to the LDS.
   auto read_frags_from = [&](const unsigned char* sa, int kk, int buf) {
     const unsigned char* sb = sa + BM * Cfg::kRowBytes;
     const uint32_t c = 2 * kk + frag_half;
@@ -378,35 +378,25 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   auto tile_body = [&](int kt, auto load_c) {
     constexpr int LOAD = decltype(load_c)::value;
     static_assert(kSteps % 2 == 0, "fragment sets alternate per step");
-    const int next = kt + Cfg::STAGES - 1;
-    if constexpr (LOAD == 2) {
-#pragma unroll
-      for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(fill, j, next);
-    }
+    const int next = kt + Cfg::STAGES;
     const unsigned char* sa = smem + cur * Cfg::kStageBytes;
     const unsigned char* na = smem + (cur + 1 == Cfg::STAGES ? 0 : cur + 1) * Cfg::kStageBytes;
     // Explicit order, fenced so the compiler keeps it: in every step, group
-    // g is MFMA g, then copy g (step 0 of a loading tile), then fragment
-    // read g for the next step. No MFMA moves into another step, so each
-    // accumulator is updated once per step and the reads have a step's
-    // worth of MFMAs to land in.
+    // g is MFMA g, then fragment read g for the next step. No MFMA moves
+    // into another step, so each accumulator is updated once per step and
+    // the reads have a step's worth of MFMAs to land in.
     static_for<kSteps>([&](auto kkc) {
       constexpr int kk = decltype(kkc)::value;
       constexpr bool kLast = kk + 1 == kSteps;
       constexpr int kReads = kLast ? 0 : Cfg::kFragM + Cfg::kFragN;
-      constexpr int kDmas = LOAD == 1 && kk == 0 ? Cfg::kSlabsPerWave : 0;
       constexpr int kRows = kLast ? Cfg::kFragM / 2 : Cfg::kFragM;
       constexpr int kMf = kRows * Cfg::kFragN;
       static_for<kMf>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
         mfma(kk, std::integral_constant<int, g / Cfg::kFragN>{},
              std::integral_constant<int, g % Cfg::kFragN>{});
-        if constexpr (g < kDmas) dma(fill, g, next);
         if constexpr (g < kReads) read_frag(sa, kk + 1, (kk + 1) & 1, gc);
         __builtin_amdgcn_sched_barrier(0);
-      });
-      static_for<(kDmas > kMf ? kDmas - kMf : 0)>([&](auto dc) {
-        dma(fill, kMf + decltype(dc)::value, next);
       });
       static_for<(kReads > kMf ? kReads - kMf : 0)>([&](auto rc) {
         read_frag(sa, kk + 1, (kk + 1) & 1,
@@ -424,11 +414,22 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
         __builtin_amdgcn_sched_barrier(0);
         constexpr int kRest = (Cfg::kFragM - kRows) * Cfg::kFragN;
         constexpr int kNext = Cfg::kFragM + Cfg::kFragN;
+        // the copies of K tile kt + STAGES, into this tile's buffer (every
+        // wave has read it once past the barrier), two or so after each MFMA
+        constexpr int kEarlyDmas = LOAD != 0 ? Cfg::kSlabsPerWave : 0;
+        constexpr int kPer = (kEarlyDmas + kRest - 1) / kRest;
         static_for<kRest>([&](auto gc) {
           constexpr int g = decltype(gc)::value;
           if constexpr (g < kNext) read_frag(na, 0, 0, gc);
           mfma(kk, std::integral_constant<int, kRows + g / Cfg::kFragN>{},
                std::integral_constant<int, g % Cfg::kFragN>{});
+          static_for<kPer>([&](auto dc) {
+            constexpr int j = g * kPer + decltype(dc)::value;
+            if constexpr (j < kEarlyDmas) {
+              if constexpr (LOAD == 2) dma_tail(cur, j, next);
+              else dma(cur, j, next);
+            }
+          });
           __builtin_amdgcn_sched_barrier(0);
         });
         static_for<(kNext > kRest ? kNext - kRest : 0)>([&](auto rc) {
@@ -438,11 +439,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
       }
     });
     cur = cur + 1 == Cfg::STAGES ? 0 : cur + 1;
-    fill = fill + 1 == Cfg::STAGES ? 0 : fill + 1;
   };
 
 #pragma unroll
-  for (int s = 0; s < Cfg::STAGES - 1; ++s) {
+  for (int s = 0; s < Cfg::STAGES; ++s) {
     if (s < kfull) {
 #pragma unroll
       for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma(s, j, s);
@@ -451,18 +451,21 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
       for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(s, j, s);
     }
   }
-  // Three phases, each a loop over one instance of the body (an if/else of
-  // two instances inside one loop costs registers): copies of whole tiles;
-  // the copy of the partial last tile, if K has one and it was not already
-  // issued by the prologue; no copies.
+  // The prologue copies tiles 0 .. STAGES - 1. Then three phases, each a
+  // loop over one instance of the body (an if/else of two instances inside
+  // one loop costs registers): bodies that copy a whole tile; the one that
+  // copies the partial last tile, if K has one the prologue did not cover;
+  // bodies that copy nothing.
   if (ktiles > 0) {
-    wait_for(0);
+    // tile 0 has landed (the prologue issued up to STAGES tiles)
+    if (Cfg::STAGES - 1 < ktiles) wait_vmcnt<(Cfg::STAGES - 1) * Cfg::kSlabsPerWave>();
+    else wait_vmcnt<0>();
     barrier_lds();
     read_frags_from(smem, 0, 0);
   }
   int kt = 0;
-  for (; kt + Cfg::STAGES - 1 < kfull; ++kt) tile_body(kt, std::integral_constant<int, 1>{});
-  if (kfull < ktiles && kt + Cfg::STAGES - 1 == kfull) {
+  for (; kt + Cfg::STAGES < kfull; ++kt) tile_body(kt, std::integral_constant<int, 1>{});
+  if (kfull < ktiles && kt + Cfg::STAGES == kfull) {
     tile_body(kt, std::integral_constant<int, 2>{});
     ++kt;
   }
