@@ -238,6 +238,9 @@ int check_common(const void* y, int32_t dtype, int64_t n) {
 
 uint32_t vec_alignment(int32_t dtype) { return dtype == ASR_F32 ? 16 : 8; }
 
+// The draws are formed in binary32: a parameter must be a finite binary32 value.
+bool fits_f32(double v) { return std::isfinite(v) && std::fabs(v) <= 3.4028234663852886e38; }
+
 }  // namespace
 
 extern "C" {
@@ -245,8 +248,8 @@ extern "C" {
 int asr_random_uniform(void* out, int32_t dtype, int64_t n, double low, double high,
                        uint32_t seed, uint32_t step, uint64_t base_index, void* stream) {
   if (int s = check_common(out, dtype, n)) return s;
-  if (!std::isfinite(low) || !std::isfinite(high) || !std::isfinite(high - low))
-    return fail(ASR_EINVAL, "low and high must be finite");
+  if (!fits_f32(low) || !fits_f32(high) || !fits_f32(high - low))
+    return fail(ASR_EINVAL, "low, high and high - low must be finite in binary32");
   if (n == 0) return ok();
   asr_rng::Params P{};
   P.y = out;
@@ -263,8 +266,8 @@ int asr_random_uniform(void* out, int32_t dtype, int64_t n, double low, double h
 int asr_random_normal(void* out, int32_t dtype, int64_t n, double mean, double std,
                       uint32_t seed, uint32_t step, uint64_t base_index, void* stream) {
   if (int s = check_common(out, dtype, n)) return s;
-  if (!std::isfinite(mean) || !std::isfinite(std) || std < 0.0)
-    return fail(ASR_EINVAL, "mean must be finite and std finite and >= 0");
+  if (!fits_f32(mean) || !fits_f32(std) || std < 0.0)
+    return fail(ASR_EINVAL, "mean and std must be finite in binary32, std >= 0");
   if (n == 0) return ok();
   asr_rng::Params P{};
   P.y = out;

@@ -244,7 +244,8 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b,
  * their own base_index reproduces the whole bit for bit.
  *
  * asr_random_uniform: out[i] = f32(low) + f32(high - low) * U,
- *   U = (W >> 8) * 2**-24 in [0, 1). low, high finite.
+ *   U = (W >> 8) * 2**-24 in [0, 1). low, high and high - low finite in
+ *   binary32.
  * asr_random_normal: Box-Muller on position pairs (2q, 2q + 1):
  *   u1 = ((W(2q) >> 8) + 1) * 2**-24, u2 = (W(2q + 1) >> 8) * 2**-24,
  *   r = sqrt(-2 ln u1); z(2q) = r cos(2 pi u2), z(2q + 1) = r sin(2 pi u2);
@@ -253,7 +254,7 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b,
  *   v_sin_f32, v_cos_f32), whose error over every input they can receive
  *   here is measured by asr_box_muller_given_words; values are reproducible
  *   on this library but not bit-identical to other implementations.
- *   mean finite, std finite and >= 0.
+ *   mean and std finite in binary32, std >= 0.
  * asr_dropout: drop probability p in [0, 1). Element i is dropped when
  *   W < floor(p * 2**32); y[i] = x[i] * (dropped ? 0 : f32(1 / (1 - p))), one
  *   binary32 multiply (a dropped Inf or NaN gives NaN, a dropped negative

@@ -199,6 +199,11 @@ def test_random_argument_errors():
     assert _status(u, 0x1000, E.ASR_F32, 16, -1e308, 1e308, 1, 2, 0, None) == E.ASR_EINVAL
     assert _status(nrm, 0x1000, E.ASR_F32, 16, 0.0, -1.0, 1, 2, 0, None) == E.ASR_EINVAL
     assert _status(nrm, 0x1000, E.ASR_F32, 16, float("nan"), 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    # parameters are used in binary32: finite doubles beyond its range are refused
+    assert _status(u, 0x1000, E.ASR_F32, 16, -1e39, 0.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(u, 0x1000, E.ASR_F32, 16, -3e38, 3e38, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(nrm, 0x1000, E.ASR_F32, 16, 1e39, 1.0, 1, 2, 0, None) == E.ASR_EINVAL
+    assert _status(nrm, 0x1000, E.ASR_F32, 16, 0.0, 1e39, 1, 2, 0, None) == E.ASR_EINVAL
     assert _status(d, 0x1000, 0x2000, None, E.ASR_F32, 16, 1.0, 1, 2, 0, None) == E.ASR_EINVAL
     assert _status(d, 0x1000, 0x2000, None, E.ASR_F32, 16, -0.1, 1, 2, 0, None) == E.ASR_EINVAL
     assert _status(d, 0x1000, 0x2000, None, E.ASR_F32, 16, float("nan"), 1, 2, 0, None) == E.ASR_EINVAL
