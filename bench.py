@@ -242,7 +242,7 @@ def _time_launches(torch, stream, fn, steps):
     return wall / steps, sum(a.elapsed_time(b) for a, b in events) / steps
 
 
-def gemm_cpu_baseline(m, n, k, rows=1024):
+def gemm_cpu_baseline(m, n, k, rows=4096):
     """The oracle's GEMM (binary64 product, then SR of the f32 result) on
     `rows` rows of the same shape, timed on the host (the product runs on the
     BLAS threads, the rounding on one)."""
