@@ -99,12 +99,17 @@ struct TileCfg {
   static constexpr int kChunks = BK / 8;                   // 16-byte chunks per row
   static constexpr int kSlabRows = kDmaBytes / kRowBytes;  // rows per wave-wide DMA
   static constexpr int kSlabs = (BM + BN) / kSlabRows;
-  static constexpr int kSlabsPerWave = kSlabs / kWaves;    // DMAs per lane per stage
+  // Waves that issue the copies: one per SIMD (waves 0 .. 3; wave w runs on
+  // SIMD w % 4). With two waves per SIMD the other one keeps issuing MFMAs
+  // while its partner's copies wait to issue, instead of both stalling at
+  // once.
+  static constexpr int kCopyWaves = kWaves > 4 ? 4 : kWaves;
+  static constexpr int kSlabsPerWave = kSlabs / kCopyWaves;  // DMAs per copying lane per stage
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
-  static_assert(kSlabs % kWaves == 0, "every wave fills the same number of slabs");
+  static_assert(kSlabs % kCopyWaves == 0, "every copying wave fills the same number of slabs");
   static_assert(BM % kSlabRows == 0, "a slab lies in A or in B");
   static_assert(STAGES >= 2 && kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -272,14 +277,16 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   // of A or B are clamped to the last row: they only feed outputs that are
   // not stored.
   constexpr int kChunks = Cfg::kChunks;
-  constexpr int kSlabsA = BM / Cfg::kSlabRows / Cfg::kWaves;
-  static_assert((BM / Cfg::kSlabRows) % Cfg::kWaves == 0, "A slabs split evenly over waves");
+  constexpr int kCopiers = Cfg::kCopyWaves;
+  constexpr int kSlabsA = BM / Cfg::kSlabRows / kCopiers;
+  static_assert((BM / Cfg::kSlabRows) % kCopiers == 0, "A slabs split evenly over waves");
+  const bool copier = kCopiers == Cfg::kWaves || wave < static_cast<uint32_t>(kCopiers);
   const int32_t last_a = args.m - 1 - static_cast<int32_t>(m0);
   const int32_t last_b = args.n - 1 - static_cast<int32_t>(n0);
   uint32_t voff[Cfg::kSlabsPerWave];
 #pragma unroll
   for (int j = 0; j < Cfg::kSlabsPerWave; ++j) {
-    const uint32_t row = (wave + j * Cfg::kWaves) * Cfg::kSlabRows + lane / kChunks;
+    const uint32_t row = (wave + j * kCopiers) * Cfg::kSlabRows + lane / kChunks;
     const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);  // the XOR is its own inverse
     if (j < kSlabsA)
       voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row), last_a)) *
@@ -299,14 +306,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
     const char* base = (j < kSlabsA ? a_tile : b_tile) + static_cast<int64_t>(kt) * Cfg::kRowBytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         buffer_of(base),
-        (lds_void_ptr)(smem + stage * Cfg::kStageBytes + (wave + j * Cfg::kWaves) * kDmaBytes),
+        (lds_void_ptr)(smem + stage * Cfg::kStageBytes + (wave + j * kCopiers) * kDmaBytes),
         16, off, 0, 0, 0);
   };
   auto dma = [&](int stage, int j, int kt) { dma_off(stage, j, kt, voff[j]); };
   // The last K tile when K is not a multiple of BK: chunks at or past K read
   // zeros (K is a multiple of 8, so a chunk is wholly inside or outside).
   auto dma_tail = [&](int stage, int j, int kt) {
-    const uint32_t row = (wave + j * Cfg::kWaves) * Cfg::kSlabRows + lane / kChunks;
+    const uint32_t row = (wave + j * kCopiers) * Cfg::kSlabRows + lane / kChunks;
     const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);
     const int k = kt * Cfg::BK + static_cast<int>(c) * 8;
     dma_off(stage, j, kt, k < args.k ? voff[j] : kOutOfRange);
@@ -426,8 +433,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
           static_for<kPer>([&](auto dc) {
             constexpr int j = g * kPer + decltype(dc)::value;
             if constexpr (j < kEarlyDmas) {
-              if constexpr (LOAD == 2) dma_tail(cur, j, next);
-              else dma(cur, j, next);
+              if (copier) {
+                if constexpr (LOAD == 2) dma_tail(cur, j, next);
+                else dma(cur, j, next);
+              }
             }
           });
           __builtin_amdgcn_sched_barrier(0);
@@ -443,7 +452,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 
 #pragma unroll
   for (int s = 0; s < Cfg::STAGES; ++s) {
-    if (s < kfull) {
+    if (!copier) {
+    } else if (s < kfull) {
 #pragma unroll
       for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma(s, j, s);
     } else if (s < ktiles) {
