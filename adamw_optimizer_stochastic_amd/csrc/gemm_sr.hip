@@ -47,6 +47,12 @@
 //   * Tiles are handed to XCDs in contiguous ranges (workgroup b runs on XCD
 //     b % 8) and grouped along M inside each range, so the workgroups that
 //     share an L2 also share A and B panels.
+//   * With more big tiles than CUs the launch is persistent: one workgroup
+//     per CU runs output tiles b, b + #CUs, ... (the same order), and the
+//     ring carries on across them: the next tile's first two K tiles are
+//     copied during the current tile's last two, so a tile starts with its
+//     operands in LDS, and its waits leave the previous tile's output stores
+//     in flight (vector-memory operations complete in issue order).
 #include "device.hpp"
 #include "status.hpp"
 
@@ -254,7 +260,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& args, int64_t m, int64
   }
 }
 
-template <typename Cfg, int ROUND, bool F32OUT>
+template <typename Cfg, int ROUND, bool F32OUT, bool PERSIST>
 __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN;
   __shared__ __align__(1024) unsigned char smem[Cfg::kLdsBytes];
@@ -263,10 +269,6 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   // The wave index as a scalar: every LDS destination and global base below
   // is then uniform and lives in scalar registers.
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t tm, tn;
-  tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
-  const int64_t m0 = static_cast<int64_t>(tm) * BM;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
   // ---- this lane's share of the global -> LDS copies. Slab j of this wave
   // is rows slab * kSlabRows .. + kSlabRows - 1 of the stage (slab = wave +
@@ -281,22 +283,40 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   constexpr int kSlabsA = BM / Cfg::kSlabRows / kCopiers;
   static_assert((BM / Cfg::kSlabRows) % kCopiers == 0, "A slabs split evenly over waves");
   const bool copier = kCopiers == Cfg::kWaves || wave < static_cast<uint32_t>(kCopiers);
-  const int32_t last_a = args.m - 1 - static_cast<int32_t>(m0);
-  const int32_t last_b = args.n - 1 - static_cast<int32_t>(n0);
+  // The tile the copies fetch (origin m0, n0): the workgroup's current tile,
+  // and in the persistent form, during the current tile's last STAGES K
+  // tiles, the next one.
+  int64_t m0 = 0, n0 = 0;
   uint32_t voff[Cfg::kSlabsPerWave];
+  const char* a_tile = nullptr;
+  const char* b_tile = nullptr;
+  auto aim_copies = [&](uint32_t tile) {
+    uint32_t tm, tn;
+    tile_of_block(tile, args.tiles_m, args.tiles_n, tm, tn);
+    m0 = static_cast<int64_t>(tm) * BM;
+    n0 = static_cast<int64_t>(tn) * BN;
+    const int32_t last_a = args.m - 1 - static_cast<int32_t>(m0);
+    const int32_t last_b = args.n - 1 - static_cast<int32_t>(n0);
 #pragma unroll
-  for (int j = 0; j < Cfg::kSlabsPerWave; ++j) {
-    const uint32_t row = (wave + j * kCopiers) * Cfg::kSlabRows + lane / kChunks;
-    const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);  // the XOR is its own inverse
-    if (j < kSlabsA)
-      voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row), last_a)) *
-                     static_cast<uint32_t>(args.lda) + c * 8) * 2;
-    else
-      voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row) - BM, last_b)) *
-                     static_cast<uint32_t>(args.ldb) + c * 8) * 2;
-  }
-  const char* a_tile = reinterpret_cast<const char*>(args.a + m0 * args.lda);
-  const char* b_tile = reinterpret_cast<const char*>(args.b + n0 * args.ldb);
+    for (int j = 0; j < Cfg::kSlabsPerWave; ++j) {
+      const uint32_t row = (wave + j * kCopiers) * Cfg::kSlabRows + lane / kChunks;
+      const uint32_t c = Cfg::chunk_pos(row, lane % kChunks);  // the XOR is its own inverse
+      if (j < kSlabsA)
+        voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row), last_a)) *
+                       static_cast<uint32_t>(args.lda) + c * 8) * 2;
+      else
+        voff[j] = (static_cast<uint32_t>(row_clamp(static_cast<int32_t>(row) - BM, last_b)) *
+                       static_cast<uint32_t>(args.ldb) + c * 8) * 2;
+    }
+    a_tile = reinterpret_cast<const char*>(args.a + m0 * args.lda);
+    b_tile = reinterpret_cast<const char*>(args.b + n0 * args.ldb);
+  };
+  uint32_t tile = blockIdx.x;
+  aim_copies(tile);
+  bool has_next = false;  // persistent form: this workgroup has another output tile
+  // persistent form: the previous output tile's kStoresPerWave stores were
+  // issued after this tile's first STAGES K tiles of copies
+  bool stores_behind = false;
 
   // Copy of slab j of K tile kt into LDS buffer `stage`: a buffer load to
   // LDS (buffer_load_dwordx4 ... lds) from a resource at the tile's first
@@ -320,10 +340,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   };
 
   f32x16 acc[Cfg::kFragM][Cfg::kFragN];
-#pragma unroll
-  for (int i = 0; i < Cfg::kFragM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::kFragN; ++j) acc[i][j] = f32x16{};
+  // Vector-memory instructions one wave's epilogue issues for a tile that
+  // lies wholly inside C: one 8-byte store per 4 outputs, more with the f32
+  // copy or unaligned C (never fewer).
+  constexpr int kStoresPerWave = Cfg::kFragM * Cfg::kFragN * 4;
+  static_assert((Cfg::STAGES - 1) * Cfg::kSlabsPerWave + kStoresPerWave < 64, "vmcnt range");
 
   const uint32_t wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const uint32_t frag_row = lane & 31u, frag_half = lane >> 5;
@@ -341,7 +362,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
 
   // LOAD (the copies a tile body issues, of tile kt + STAGES): 0 = none,
-  // 1 = a whole tile, 2 = the partial last tile.
+  // 1 = a whole tile, 2 = the partial last tile, 3 = a whole K tile of the
+  // next output tile (K tile kt + STAGES - ktiles; persistent form).
   // The barrier sits inside the last MFMA step of each tile.
   // Half of that step's MFMAs are issued, then the wave waits for tile
   // kt + 1, passes the barrier, and issues tile kt + 1's first fragment
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   auto tile_body = [&](int kt, auto load_c) {
     constexpr int LOAD = decltype(load_c)::value;
     static_assert(kSteps % 2 == 0, "fragment sets alternate per step");
-    const int next = kt + Cfg::STAGES;
+    const int next = kt + Cfg::STAGES - (LOAD == 3 ? ktiles : 0);
     const unsigned char* sa = smem + cur * Cfg::kStageBytes;
     const unsigned char* na = smem + (cur + 1 == Cfg::STAGES ? 0 : cur + 1) * Cfg::kStageBytes;
     // Explicit order, fenced so the compiler keeps it: in every step, group
@@ -415,8 +437,15 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
         // a read of the next tile's first step (harmless after the last
         // tile: the LDS is only read, and the values are not used)
         if (kt + 1 < ktiles) {
-          wait_for(kt + 1);
+          // (K tile 1 of a tile whose predecessor's stores follow its copies:
+          // those stores may stay outstanding)
+          if (PERSIST && kt == 0 && stores_behind)
+            wait_vmcnt<(Cfg::STAGES - 2) * Cfg::kSlabsPerWave + kStoresPerWave>();
+          else
+            wait_for(kt + 1);
           barrier_lds();  // tile kt + 1 visible; every wave is done with tile kt - 1's buffer
+        } else if constexpr (LOAD == 3) {
+          barrier_lds();  // every wave is done with this buffer before the next tile's copies
         }
         __builtin_amdgcn_sched_barrier(0);
         constexpr int kRest = (Cfg::kFragM - kRows) * Cfg::kFragN;
@@ -433,7 +462,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
           static_for<kPer>([&](auto dc) {
             constexpr int j = g * kPer + decltype(dc)::value;
             if constexpr (j < kEarlyDmas) {
-              if (copier) {
+              if (copier && (LOAD != 3 || has_next)) {
                 if constexpr (LOAD == 2) dma_tail(cur, j, next);
                 else dma(cur, j, next);
               }
@@ -450,6 +479,22 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
     cur = cur + 1 == Cfg::STAGES ? 0 : cur + 1;
   };
 
+  static_assert(!PERSIST || Cfg::STAGES == 2, "the persistent form assumes a 2-deep ring");
+  // The prologue copies K tiles 0 .. STAGES - 1. Then, per output tile,
+  // three phases, each a loop over one instance of the body (an if/else of
+  // two instances inside one loop costs registers): bodies that copy a
+  // whole K tile; the one that copies the partial last K tile, if K has one
+  // the prologue did not cover; bodies that copy the next output tile's
+  // first K tiles (persistent form) or nothing.
+  //
+  // Persistent form (one workgroup per CU, output tiles blockIdx.x,
+  // blockIdx.x + gridDim.x, ...; needs kfull >= STAGES): the ring carries on
+  // across output tiles, so the next tile's first K tiles are in flight
+  // during this tile's last K tiles and its epilogue. Vector-memory
+  // operations complete in issue order, so the next tile's waits for its K
+  // tiles 0 and 1 may leave this tile's stores outstanding: exactly
+  // kStoresPerWave of them when the tile is interior; otherwise they also
+  // wait for the stores.
 #pragma unroll
   for (int s = 0; s < Cfg::STAGES; ++s) {
     if (!copier) {
@@ -461,46 +506,81 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
       for (int j = 0; j < Cfg::kSlabsPerWave; ++j) dma_tail(s, j, s);
     }
   }
-  // The prologue copies tiles 0 .. STAGES - 1. Then three phases, each a
-  // loop over one instance of the body (an if/else of two instances inside
-  // one loop costs registers): bodies that copy a whole tile; the one that
-  // copies the partial last tile, if K has one the prologue did not cover;
-  // bodies that copy nothing.
-  if (ktiles > 0) {
-    // tile 0 has landed (the prologue issued up to STAGES tiles)
-    if (Cfg::STAGES - 1 < ktiles) wait_vmcnt<(Cfg::STAGES - 1) * Cfg::kSlabsPerWave>();
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < Cfg::kFragM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::kFragN; ++j) acc[i][j] = f32x16{};
+  };
+  // K tile 0 has landed (up to STAGES K tiles were issued, then maybe the
+  // previous output tile's stores): make it visible, read its first step.
+  auto start_tile = [&]() {
+    if (stores_behind) wait_vmcnt<(Cfg::STAGES - 1) * Cfg::kSlabsPerWave + kStoresPerWave>();
+    else if (Cfg::STAGES - 1 < ktiles) wait_vmcnt<(Cfg::STAGES - 1) * Cfg::kSlabsPerWave>();
     else wait_vmcnt<0>();
     barrier_lds();
-    read_frags_from(smem, 0, 0);
-  }
-  int kt = 0;
-  for (; kt + Cfg::STAGES < kfull; ++kt) tile_body(kt, std::integral_constant<int, 1>{});
-  if (kfull < ktiles && kt + Cfg::STAGES == kfull) {
-    tile_body(kt, std::integral_constant<int, 2>{});
-    ++kt;
-  }
-  for (; kt < ktiles; ++kt) tile_body(kt, std::integral_constant<int, 0>{});
-
-  // ---- epilogue. acc[i][j] register r of lane l holds C[m][n] with
-  // m = row base + l%32 and n = column base + 8*(r/4) + 4*(l/32) + r%4.
-  // Compile-time loops keep every accumulator index constant (a runtime
-  // index would move the accumulators to scratch memory).
-  static_for<Cfg::kFragM>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int64_t m = m0 + wm * Cfg::WM + i * 32 + frag_row;
-    if (m >= args.m) return;
-    static_for<Cfg::kFragN>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      static_for<4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        const int64_t n = n0 + wn * Cfg::WN + j * 32 + 8 * q + 4 * frag_half;
-        if (n >= args.n) return;
-        const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                            acc[i][j][4 * q + 3]};
-        store_out<ROUND, F32OUT>(args, m, n, x);
+    read_frags_from(smem + cur * Cfg::kStageBytes, 0, 0);
+  };
+  // Phases 1 and 2; returns the first K tile of the last phase.
+  auto own_copies = [&]() {
+    int kt = 0;
+    for (; kt + Cfg::STAGES < kfull; ++kt) tile_body(kt, std::integral_constant<int, 1>{});
+    if (kfull < ktiles && kt + Cfg::STAGES == kfull) {
+      tile_body(kt, std::integral_constant<int, 2>{});
+      ++kt;
+    }
+    return kt;
+  };
+  // acc[i][j] register r of lane l holds C[m][n] with m = row base + l%32
+  // and n = column base + 8*(r/4) + 4*(l/32) + r%4. Compile-time loops keep
+  // every accumulator index constant (a runtime index would move the
+  // accumulators to scratch memory).
+  auto epilogue = [&](int64_t em0, int64_t en0, uint32_t e_row, uint32_t e_half) {
+    static_for<Cfg::kFragM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int64_t m = em0 + wm * Cfg::WM + i * 32 + e_row;
+      if (m >= args.m) return;
+      static_for<Cfg::kFragN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        static_for<4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const int64_t n = en0 + wn * Cfg::WN + j * 32 + 8 * q + 4 * e_half;
+          if (n >= args.n) return;
+          const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
+          store_out<ROUND, F32OUT>(args, m, n, x);
+        });
       });
     });
-  });
+  };
+
+  if constexpr (!PERSIST) {
+    zero_acc();
+    if (ktiles > 0) start_tile();
+    int kt = own_copies();
+    for (; kt < ktiles; ++kt) tile_body(kt, std::integral_constant<int, 0>{});
+    epilogue(m0, n0, frag_row, frag_half);
+  } else {
+    for (;;) {
+      const int64_t em0 = m0, en0 = n0;  // this output tile
+      const uint32_t next_tile = tile + gridDim.x;
+      has_next = next_tile < args.tiles_m * args.tiles_n;
+      zero_acc();
+      start_tile();  // (ktiles >= STAGES here)
+      int kt = own_copies();
+      aim_copies(has_next ? next_tile : tile);  // (no copies are issued without a next tile)
+      for (; kt < ktiles; ++kt) tile_body(kt, std::integral_constant<int, 3>{});
+      // The lane index goes through an empty asm so that no part of the
+      // store addresses is hoisted out of the tile loop (it would stay live
+      // through the K loop).
+      uint32_t el = lane;
+      asm volatile("" : "+v"(el));
+      epilogue(em0, en0, el & 31u, el >> 5);
+      if (!has_next) break;
+      stores_behind = em0 + BM <= args.m && en0 + BN <= args.n;
+      tile = next_tile;
+    }
+  }
 }
 
 #ifndef ASR_GEMM_BIG
@@ -508,6 +588,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 #endif
 #ifndef ASR_GEMM_SMALL
 #define ASR_GEMM_SMALL 128, 128, 64, 64, 64, 2
+#endif
+#ifndef ASR_GEMM_PERSIST
+#define ASR_GEMM_PERSIST 1
 #endif
 using Big = TileCfg<ASR_GEMM_BIG>;      // 8 waves, 2 per SIMD
 using Small = TileCfg<ASR_GEMM_SMALL>;  // 4 waves, for grids too small for Big
@@ -525,25 +608,43 @@ bool aligned_to(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
-template <typename Cfg, int ROUND, bool F32OUT>
-hipError_t launch_gemm(asr_gemm::GemmArgs args, hipStream_t stream) {
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Launches one workgroup per output tile, or with `persist_grid` > 0 that
+// many workgroups, each looping over output tiles.
+template <typename Cfg, int ROUND, bool F32OUT, bool PERSIST>
+hipError_t launch_gemm(asr_gemm::GemmArgs args, uint32_t persist_grid, hipStream_t stream) {
   args.tiles_m = static_cast<uint32_t>((args.m + Cfg::BM - 1) / Cfg::BM);
   args.tiles_n = static_cast<uint32_t>((args.n + Cfg::BN - 1) / Cfg::BN);
   const uint64_t tiles = static_cast<uint64_t>(args.tiles_m) * args.tiles_n;
+  const uint32_t grid = PERSIST ? persist_grid : static_cast<uint32_t>(tiles);
   void* argv[] = {&args};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&asr_gemm::gemm_bf16<Cfg, ROUND, F32OUT>),
-      dim3(static_cast<uint32_t>(tiles)), dim3(Cfg::kThreads), argv, 0, stream);
+      reinterpret_cast<const void*>(&asr_gemm::gemm_bf16<Cfg, ROUND, F32OUT, PERSIST>),
+      dim3(grid), dim3(Cfg::kThreads), argv, 0, stream);
 }
 
-template <typename Cfg>
-hipError_t dispatch(const asr_gemm::GemmArgs& args, int32_t rounding, hipStream_t stream) {
+template <typename Cfg, bool PERSIST>
+hipError_t dispatch(const asr_gemm::GemmArgs& args, int32_t rounding, uint32_t persist_grid,
+                    hipStream_t stream) {
   const bool f32 = args.c32 != nullptr;
   if (rounding == ASR_ROUND_SR)
-    return f32 ? launch_gemm<Cfg, ASR_ROUND_SR, true>(args, stream)
-               : launch_gemm<Cfg, ASR_ROUND_SR, false>(args, stream);
-  return f32 ? launch_gemm<Cfg, ASR_ROUND_RN, true>(args, stream)
-             : launch_gemm<Cfg, ASR_ROUND_RN, false>(args, stream);
+    return f32 ? launch_gemm<Cfg, ASR_ROUND_SR, true, PERSIST>(args, persist_grid, stream)
+               : launch_gemm<Cfg, ASR_ROUND_SR, false, PERSIST>(args, persist_grid, stream);
+  return f32 ? launch_gemm<Cfg, ASR_ROUND_RN, true, PERSIST>(args, persist_grid, stream)
+             : launch_gemm<Cfg, ASR_ROUND_RN, false, PERSIST>(args, persist_grid, stream);
 }
 
 }  // namespace
@@ -595,9 +696,16 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb
   if (small_tiles > 0x7FFFFFFFull) return fail(ASR_EINVAL, "gemm: too many tiles");
   hipStream_t s = static_cast<hipStream_t>(stream);
   // The big tile halves the LDS and L2 traffic per flop; it needs enough
-  // tiles to give every CU at least one.
-  const hipError_t e = big_tiles >= 256 ? dispatch<asr_gemm::Big>(args, rounding, s)
-                                        : dispatch<asr_gemm::Small>(args, rounding, s);
+  // tiles to give every CU at least one. With more tiles than CUs (one big
+  // tile fills a CU's LDS) the persistent form runs one workgroup per CU;
+  // it needs STAGES whole K tiles.
+  const int cus = cu_count();
+  const bool persist = ASR_GEMM_PERSIST && cus > 0 && big_tiles > static_cast<uint64_t>(cus) &&
+                       k / asr_gemm::Big::BK >= asr_gemm::Big::STAGES;
+  hipError_t e;
+  if (big_tiles < 256) e = dispatch<asr_gemm::Small, false>(args, rounding, 0, s);
+  else if (persist) e = dispatch<asr_gemm::Big, true>(args, rounding, static_cast<uint32_t>(cus), s);
+  else e = dispatch<asr_gemm::Big, false>(args, rounding, 0, s);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }

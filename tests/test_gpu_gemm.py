@@ -16,7 +16,9 @@
 
 Shapes span several tiles of both tile configurations (128 x 128 and
 256 x 256 workgroup tiles; the larger is used once there are at least 256
-of them) with ragged edges in M, N and K.
+of them) with ragged edges in M, N and K, and both launch forms of the
+larger one (one workgroup per tile; with more tiles than compute units, one
+persistent workgroup per compute unit running several tiles in a row).
 """
 
 import numpy as np
@@ -275,6 +277,46 @@ def test_full_size_llama_mlp_sampled(kind):
         assert within_bf16_step(got_rn, exact, bound).all()
         # SR and RN pick neighbours of the same f32 value: at most one bf16 step apart
         assert _bf16_steps_apart(got_sr.reshape(-1), got_rn.reshape(-1)).max() <= 1
+
+
+@pytest.mark.parametrize("f32", [False, True], ids=["bf16_only", "with_f32_copy"])
+def test_several_tiles_per_workgroup(f32):
+    """More 256 x 256 tiles than three per compute unit, so each workgroup of
+    the persistent launch runs three or four output tiles in a row, the next
+    tile's first K tiles fetched under the current one's last. Ragged M and N
+    (edge tiles next to interior ones) and a partial last K tile. Integer
+    operands: the f32 result and every RN output must equal the exact product
+    and the oracle's rounding of it, bit for bit; SR outputs likewise on a
+    grid that takes both edges and random rows and columns of every tile (a
+    stale or misplaced K tile spoils a whole tile)."""
+    m, n, k = 1300, 33000, 200
+    tiles = ((m + 255) // 256) * ((n + 255) // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert tiles > 3 * cus, (tiles, cus)
+    announce("gemm several tiles per workgroup", (m, n, k, f32))
+    a, b = wl.gemm_operands_host(m, n, k, "int", seed=13)
+    exact = oracle.gemm_exact(a, b).astype(np.float32)
+    seed, step, base = 99, 5, 12
+    c_sr, c32 = _run(a, b, "sr", seed, step, base, f32=f32)
+    if f32:
+        assert_bits_equal(c32.reshape(-1), exact.reshape(-1), "f32 result")
+    rng = np.random.default_rng(3)
+
+    def per_tile(extent):
+        picks = set()
+        for t0 in range(0, extent, 256):
+            t1 = min(t0 + 256, extent)
+            picks |= {t0, t1 - 1}
+            picks |= set(rng.integers(t0, t1, size=4).tolist())
+        return np.array(sorted(picks))
+
+    rows, cols = per_tile(m), per_tile(n)
+    rr, cc = np.meshgrid(rows, cols, indexing="ij")
+    want_sr = oracle.gemm_round_at(exact[rr, cc].reshape(-1), rr.reshape(-1), cc.reshape(-1), n,
+                                   seed, step, base)
+    assert_bits_equal(c_sr[rr, cc].reshape(-1), want_sr, "SR output (every tile sampled)")
+    c_rn, _ = _run(a, b, "rn", f32=f32)
+    assert_bits_equal(c_rn.reshape(-1), oracle.gemm_round(exact, "rn").reshape(-1), "RN output")
 
 
 def test_output_sharing_input_memory_is_rejected():
