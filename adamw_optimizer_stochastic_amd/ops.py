@@ -6,6 +6,8 @@ HIP stream of the tensors' device. All arithmetic runs in the library's
 kernels; there is no CPU path.
 """
 
+import operator
+
 import torch
 
 from . import _abi
@@ -26,6 +28,26 @@ def _require_gpu(t, name):
 
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _uint(name, x, bits):
+    """x as a Python int in [0, 2**bits) (the C argument's range), else
+    ValueError: ctypes would otherwise wrap it silently."""
+    try:
+        v = operator.index(x)
+    except TypeError:
+        raise TypeError(f"{name} must be an integer (got {type(x).__name__})") from None
+    if not 0 <= v < (1 << bits):
+        raise ValueError(f"{name} must be in [0, 2**{bits})")
+    return v
+
+
+def _u32(name, x):
+    return _uint(name, x, 32)
+
+
+def _u64(name, x):
+    return _uint(name, x, 64)
 
 
 def check_disjoint(spans):
@@ -69,6 +91,10 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
         raise ValueError("all lists must have the same length")
     if rounding not in ROUNDING_CODE:
         raise ValueError("rounding must be 'sr' or 'rn'")
+    seed = _u32("seed", seed)
+    step = operator.index(step)
+    if not 1 <= step < (1 << 32):
+        raise ValueError("step must be in [1, 2**32 - 1]")
     if n == 0:
         return
     device = params[0].device
@@ -85,7 +111,7 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
         if not (p.numel() == g.numel() == m.numel() == v.numel()):
             raise ValueError(f"tensor {i}: param, grad and states differ in size")
         descs.append(_abi.AsrTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
-                                    p.numel(), int(b) & 0xFFFFFFFFFFFFFFFF,
+                                    p.numel(), _u64(f"base_indices[{i}]", b),
                                     _DTYPE_CODE[p.dtype], _DTYPE_CODE[g.dtype]))
     # p, m and v are written in place, so no buffer may share memory with another
     check_disjoint((t.data_ptr(), t.numel() * t.element_size(), f"{name}[{i}]")
@@ -98,7 +124,7 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
         raise ValueError(f"workspace must be on {device} and hold {need} bytes")
     with torch.cuda.device(device):
         _abi.asr_adamw_step(descs, float(lr), float(beta1), float(beta2), float(eps),
-                            float(weight_decay), int(step), int(seed), ROUNDING_CODE[rounding],
+                            float(weight_decay), step, seed, ROUNDING_CODE[rounding],
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream(device))
 
@@ -107,15 +133,15 @@ def philox_4x32_fill(n_counters, counter_base, seed, step, counter_upper=0, *, o
                      device="cuda"):
     """Words of n_counters Philox4x32-10 calls as an int32 tensor of 4*n_counters
     (reinterpret as uint32)."""
+    args = (_u64("counter_base", counter_base), _u64("counter_upper", counter_upper),
+            _u32("seed", seed), _u32("step", step))
     if out is None:
         out = torch.empty(4 * n_counters, dtype=torch.int32, device=device)
     _require_gpu(out, "out")
     if out.dtype != torch.int32 or out.numel() != 4 * n_counters:
         raise ValueError("out must be int32 with 4*n_counters elements")
     with torch.cuda.device(out.device):
-        _abi.asr_philox_4x32_fill(out.data_ptr(), n_counters, int(counter_base) % (1 << 64),
-                                  int(counter_upper) % (1 << 64), int(seed), int(step),
-                                  _stream(out.device))
+        _abi.asr_philox_4x32_fill(out.data_ptr(), n_counters, *args, _stream(out.device))
     return out
 
 
@@ -134,10 +160,10 @@ def _convert_args(x, out):
 
 def cvt_f32_bf16_sr(x, seed, step, base_index=0, *, out=None):
     """Stochastic rounding f32 -> bf16 (element i at position base_index + i)."""
+    key = (_u32("seed", seed), _u32("step", step), _u64("base_index", base_index))
     out = _convert_args(x, out)
     with torch.cuda.device(x.device):
-        _abi.asr_cvt_f32_bf16_sr(x.data_ptr(), out.data_ptr(), x.numel(), int(seed), int(step),
-                                 int(base_index) % (1 << 64), _stream(x.device))
+        _abi.asr_cvt_f32_bf16_sr(x.data_ptr(), out.data_ptr(), x.numel(), *key, _stream(x.device))
     return out
 
 
@@ -170,6 +196,7 @@ def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, ou
         raise ValueError(f"K mismatch: a is {tuple(a.shape)}, b is {tuple(b.shape)}")
     if rounding not in ("rn", "sr"):
         raise ValueError("rounding must be 'rn' or 'sr'")
+    key = (_u32("seed", seed), _u32("step", step), _u64("base_index", base_index))
     m, k = a.shape
     n = b.shape[0]
     if out is None:
@@ -195,8 +222,7 @@ def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, ou
     code = ASR_ROUND_SR if rounding == "sr" else ASR_ROUND_RN
     with torch.cuda.device(a.device):
         _abi.asr_gemm_bf16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, f32_ptr,
-                           m, n, k, code, int(seed), int(step), int(base_index) % (1 << 64),
-                           _stream(a.device))
+                           m, n, k, code, *key, _stream(a.device))
     return out
 
 

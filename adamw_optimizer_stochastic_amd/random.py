@@ -17,19 +17,17 @@ binary32 value.
 import torch
 
 from . import _abi, ops
-from .ops import _require_gpu, _stream, _DTYPE_CODE
+from .ops import _require_gpu, _stream, _DTYPE_CODE, _u32 as _u32_named, _u64 as _u64_named
 
 __all__ = ["philox_4x32", "uniform", "normal", "uniform_", "normal_", "dropout"]
 
 
 def _u64(x):
-    return int(x) % (1 << 64)
+    return _u64_named("base_index", x)
 
 
 def _u32(name, x):
-    if not (isinstance(x, int) and 0 <= x < (1 << 32)):
-        raise ValueError(f"{name} must be an integer in [0, 2**32)")
-    return x
+    return _u32_named(name, x)
 
 
 def _code(t):

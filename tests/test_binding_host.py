@@ -1,0 +1,51 @@
+"""Argument checks of the Python binding that run before any GPU work.
+
+The C entry points take 32-bit seeds and steps and 64-bit stream
+positions; ctypes would wrap an out-of-range Python int without a word, so
+the binding rejects it instead."""
+
+import numpy as np
+import pytest
+import torch
+
+from adamw_optimizer_stochastic_amd import ops, random as arng
+
+
+def test_integer_ranges():
+    assert ops._u32("seed", 0) == 0
+    assert ops._u32("seed", (1 << 32) - 1) == (1 << 32) - 1
+    assert ops._u32("seed", np.uint32(7)) == 7
+    assert ops._u64("base_index", (1 << 64) - 1) == (1 << 64) - 1
+    assert ops._u64("base_index", np.int64(1 << 40)) == 1 << 40
+    for bad in (-1, 1 << 32):
+        with pytest.raises(ValueError, match="seed"):
+            ops._u32("seed", bad)
+    for bad in (-1, 1 << 64):
+        with pytest.raises(ValueError, match="base_index"):
+            ops._u64("base_index", bad)
+    with pytest.raises(TypeError):
+        ops._u32("seed", 1.0)
+
+
+def test_adamw_step_key_checked_before_launch():
+    kw = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    ops.adamw_step([], [], [], [], [], step=1, seed=0, **kw)  # nothing to do
+    with pytest.raises(ValueError, match="seed"):
+        ops.adamw_step([], [], [], [], [], step=1, seed=1 << 32, **kw)
+    for step in (0, 1 << 32):
+        with pytest.raises(ValueError, match="step"):
+            ops.adamw_step([], [], [], [], [], step=step, seed=0, **kw)
+
+
+def test_stream_arguments_checked_before_launch():
+    x = torch.zeros(8)
+    with pytest.raises(ValueError, match="seed"):
+        ops.cvt_f32_bf16_sr(x, -1, 0)
+    with pytest.raises(ValueError, match="step"):
+        ops.cvt_f32_bf16_sr(x, 0, 1 << 32)
+    with pytest.raises(ValueError, match="base_index"):
+        ops.cvt_f32_bf16_sr(x, 0, 0, base_index=-5)
+    with pytest.raises(ValueError, match="counter_base"):
+        ops.philox_4x32_fill(4, -1, 0, 0)
+    with pytest.raises(ValueError, match="base_index"):
+        arng._u64(1 << 64)   # the random module's position argument
