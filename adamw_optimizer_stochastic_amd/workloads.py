@@ -18,6 +18,10 @@ Workloads (sizes as used by the tests and the benchmark):
   * llama3_8b: the parameter list of a Llama-3-8B-shaped model (291
              tensors, 8,030,261,248 elements), bf16 matrices ~N(0, 0.02),
              RMSNorm weights 1.0, bf16 grads ~N(0, 1e-3), f32 m = v = 0.
+  * llama3_8b rank share: what one of R data-parallel ranks holds when the
+             flattened list is split into R equal contiguous ranges (the
+             ZeRO-1 layout): the pieces of the tensors inside its range,
+             each with its global base_index; values drawn as above.
   * gemm:    bf16 operands of C = A B^T. "randn": A ~N(0, 1) (activations),
              B ~N(0, 0.02) (weights); "int": integers uniform in [-8, 8]
              (every f32 partial sum is then exact). The full-size case is
@@ -58,7 +62,7 @@ def numel(shape):
 
 # ------------------------------------------------------------ host draws
 CFG_SMALL, CFG_SUBULP, CFG_F32, CFG_CONVERT, CFG_SHARDS, CFG_LLAMA = 1, 2, 3, 4, 5, 6
-CFG_GEMM = 7
+CFG_GEMM, CFG_RANK = 7, 8
 
 GEMM_LLAMA3_8B_MLP_UP = dict(m=8192, n=LLAMA3_8B["ffn"], k=LLAMA3_8B["hidden"])
 
@@ -131,6 +135,44 @@ def llama3_8b_state(device, seed=0, param_std=0.02, grad_std=1e-3, cfg=LLAMA3_8B
                         exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=device),
                         base_index=base))
         base += n
+    return out
+
+
+def llama3_8b_rank_pieces(rank, ranks, cfg=LLAMA3_8B):
+    """(name, shape, offset, length, base_index) of every piece rank `rank`
+    of `ranks` holds: the flattened list is split into `ranks` equal
+    contiguous ranges, and a tensor crossing a range boundary is cut there.
+    base_index is the piece's global position (its tensor's running total
+    of numel plus the offset)."""
+    shapes = llama3_8b_shapes(cfg)
+    total = sum(numel(s) for _, s in shapes)
+    lo, hi = total * rank // ranks, total * (rank + 1) // ranks
+    out, base = [], 0
+    for name, shape in shapes:
+        n = numel(shape)
+        a, b = max(base, lo), min(base + n, hi)
+        if a < b:
+            out.append((name, shape, a - base, b - a, a))
+        base += n
+    return out
+
+
+def llama3_8b_rank_state(device, rank, ranks, seed=0, param_std=0.02, grad_std=1e-3,
+                         cfg=LLAMA3_8B):
+    """Allocates one rank's pieces on `device`: list of dicts with name,
+    offset, param, grad, exp_avg, exp_avg_sq, base_index."""
+    gen = device_generator(device, CFG_RANK, seed, rank)
+    out = []
+    for name, shape, off, n, base in llama3_8b_rank_pieces(rank, ranks, cfg):
+        if len(shape) == 1:
+            p = torch.ones(n, dtype=torch.bfloat16, device=device)
+        else:
+            p = device_normal(n, param_std, gen, device, torch.bfloat16)
+        g = device_normal(n, grad_std, gen, device, torch.bfloat16)
+        out.append(dict(name=name, offset=off, param=p, grad=g,
+                        exp_avg=torch.zeros(n, dtype=torch.float32, device=device),
+                        exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=device),
+                        base_index=base))
     return out
 
 

@@ -8,8 +8,14 @@ in HBM), the dominant kernel's achieved HBM bandwidth against the 8 TB/s
 peak (algorithmic bytes: 22 per element), and the CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|shards|convert|gemm|rng]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload llama3_8b|llama3_8b_rank|shards|convert|gemm|rng]
     python bench.py --copy-probe      # plain copy of known size (counter scaling)
+
+The llama3_8b_rank workload is one data-parallel rank's share of the same
+list: the flattened list split into --ranks equal contiguous ranges
+(ZeRO-1), rank --rank's pieces (default 3 of 8: 42 pieces, cut at both
+ends), each with its global base_index.
 
 The gemm workload times the bf16 GEMM with the SR epilogue on the gate/up
 projection of one Llama-3-8B MLP over 8,192 tokens (M=8192, N=14336,
@@ -107,9 +113,17 @@ def traffic_from_profile(workload, n_elems):
 def run_adamw(args, torch, ops, wl):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    extra = {}
     if args.workload == "llama3_8b":
         state = wl.llama3_8b_state(dev, seed=0)
         cfg_name = "llama3_8b_param_list"
+    elif args.workload == "llama3_8b_rank":
+        state = wl.llama3_8b_rank_state(dev, args.rank, args.ranks, seed=0)
+        cfg_name = f"llama3_8b_rank{args.rank}_of_{args.ranks}"
+        extra = {"rank": args.rank, "ranks": args.ranks,
+                 "first_piece": [state[0]["name"], state[0]["offset"]],
+                 "last_piece": [state[-1]["name"], state[-1]["offset"],
+                                state[-1]["param"].numel()]}
     else:  # shards: one 268,435,456-element tensor
         n = 268435456
         gen = wl.device_generator(dev, wl.CFG_SHARDS, 0)
@@ -159,7 +173,7 @@ def run_adamw(args, torch, ops, wl):
         "config": {"workload": cfg_name, "n_tensors": len(state), "params": n_elems,
                    "param_dtype": "bf16", "grad_dtype": "bf16", "state_dtype": "f32",
                    "rounding": "sr", "algorithmic_bytes_per_param": 22,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **extra},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "adamw_sr_class<BF16,BF16,SR> (one launch per size class) + "
@@ -401,11 +415,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "shards", "convert", "gemm", "rng"])
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "llama3_8b_rank", "shards", "convert", "gemm", "rng"])
+    ap.add_argument("--rank", type=int, default=3, help="rank whose share --workload "
+                    "llama3_8b_rank times")
+    ap.add_argument("--ranks", type=int, default=8)
     ap.add_argument("--gemm-shape", default=None, help="M,N,K for --workload gemm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
+    if not 0 <= args.rank < args.ranks:
+        ap.error("--rank must be in [0, --ranks)")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the optimizer step has no cross-GPU exchange "

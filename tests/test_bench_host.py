@@ -1,6 +1,7 @@
 """Host logic of bench.py (CPU only): the kernel-source hash that keeps the
-committed HBM counters tied to the code they were taken on, and the rule that
-`traffic` is reported only while that hash (and the element count) match."""
+committed HBM counters tied to the code they were taken on, the rule that
+`traffic` is reported only while that hash (and the element count) match,
+and the rank-share split of the Llama-3-8B list."""
 
 import json
 import os
@@ -46,3 +47,27 @@ def test_committed_counters_describe_the_llama_list():
     assert doc["n_elems"] == 8030261248
     # scaled counter bytes equal the algorithmic 22 B/element to within 0.1%
     assert abs(doc["hbm_bytes_per_launch"] / (22 * doc["n_elems"]) - 1) < 1e-3
+
+
+def test_rank_pieces_partition_the_list():
+    """The ranks' pieces cover the flattened Llama-3-8B list exactly once,
+    in order, each piece inside its tensor with base_index = the tensor's
+    running total of numel + the piece's offset."""
+    from adamw_optimizer_stochastic_amd import workloads as wl
+    shapes = wl.llama3_8b_shapes()
+    starts, pos = {}, 0
+    for name, shape in shapes:
+        starts[name] = (pos, wl.numel(shape))
+        pos += wl.numel(shape)
+    for ranks in (1, 3, 8):
+        nxt = 0
+        for r in range(ranks):
+            pieces = wl.llama3_8b_rank_pieces(r, ranks)
+            assert sum(p[3] for p in pieces) in (pos // ranks, pos // ranks + 1)
+            for name, shape, off, n, base in pieces:
+                t0, tn = starts[name]
+                assert 0 <= off and off + n <= tn and n > 0
+                assert base == t0 + off == nxt
+                nxt = base + n
+        assert nxt == pos
+    assert len(wl.llama3_8b_rank_pieces(3, 8)) == 42

@@ -3,7 +3,8 @@
   * a 268,435,456-element bf16 step run whole, as 8 shards with their own
     base_index, and split at an odd element (adamw-sr page, Correctness:
     sharded and one-piece updates must agree bit for bit);
-  * one multi-tensor call over the whole Llama-3-8B-shaped list.
+  * one multi-tensor call over the whole Llama-3-8B-shaped list, and over
+    one data-parallel rank's share of it (pieces with global base_index).
 Outputs are checked bit for bit against the oracle on sampled windows and
 special positions, and by properties that hold at any size on the rest.
 """
@@ -163,6 +164,49 @@ def test_llama3_8b_list_two_steps_sampled():
         assert_bits_equal(to_host(t["param"][s:e]), p, what + " param")
         assert_bits_equal(to_host(t["exp_avg"][s:e]), m, what + " m")
         assert_bits_equal(to_host(t["exp_avg_sq"][s:e]), v, what + " v")
+    del state, lists
+
+
+def test_llama3_8b_rank_share_two_steps_sampled():
+    """One data-parallel rank's share of the Llama-3-8B list (rank 3 of 8 of
+    the flattened list, ZeRO-1 layout: 42 pieces, cut inside a tensor at
+    both ends), as the benchmark's rank workload launches it: one call, two
+    steps, each piece with its global base_index. The oracle runs both steps
+    on windows at the start, middle and end of every piece, so each piece's
+    random bits must come from its global positions."""
+    dev = torch.device("cuda", 0)
+    announce("llama3-8b rank 3/8: inputs (12 GB)")
+    state = wl.llama3_8b_rank_state(dev, 3, 8, seed=0)
+    assert len(state) == 42 and state[0]["offset"] > 0
+    assert sum(t["param"].numel() for t in state) == 8030261248 // 8
+    win = 1 << 14
+    samples = []
+    for t in state:
+        n = t["param"].numel()
+        starts = [0] if n <= 3 * win else [0, n // 2 - win // 2 + 1, n - win]
+        for s0 in starts:
+            e = min(n, s0 + (n if n <= 3 * win else win))
+            samples.append((t, s0, e, to_host(t["param"][s0:e]), to_host(t["grad"][s0:e])))
+    lists = ([t["param"] for t in state], [t["grad"] for t in state],
+             [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
+             [t["base_index"] for t in state])
+    for step in (1, 2):
+        announce("llama3-8b rank 3/8: step", step)
+        ops.adamw_step(*lists, step=step, seed=0, rounding="sr", **HP)
+    torch.cuda.synchronize()
+    announce("llama3-8b rank 3/8: oracle on", len(samples), "windows")
+    for t, s0, e, hp_, hg in samples:
+        m = np.zeros(e - s0, np.float32)
+        v = np.zeros(e - s0, np.float32)
+        p = hp_
+        for step in (1, 2):
+            p, m, v = oracle.step_tensor(p, hg, m, v, param_dtype=BF16, grad_dtype=BF16,
+                                         base_index=t["base_index"] + s0, step=step, seed=0,
+                                         **HP)
+        what = f"{t['name']}[{t['offset'] + s0}:{t['offset'] + e}]"
+        assert_bits_equal(to_host(t["param"][s0:e]), p, what + " param")
+        assert_bits_equal(to_host(t["exp_avg"][s0:e]), m, what + " m")
+        assert_bits_equal(to_host(t["exp_avg_sq"][s0:e]), v, what + " v")
     del state, lists
 
 
