@@ -41,19 +41,31 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f)
                   for f in ("adamw_sr.hip", "device.hpp")]
+GEMM_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f)
+                for f in ("gemm_sr.hip", "device.hpp")]
 
 
-def source_hash():
+def source_hash_of(files):
     """Hash of the kernel sources' code: comments and whitespace are dropped,
     so editing a comment keeps counter data valid and any code change voids it."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(f) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def source_hash():
+    """Hash of the AdamW step's kernel sources (see source_hash_of)."""
+    return source_hash_of(KERNEL_SOURCES)
+
+
+def gemm_source_hash():
+    """Hash of the GEMM's kernel sources (see source_hash_of)."""
+    return source_hash_of(GEMM_SOURCES)
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -106,6 +118,19 @@ def traffic_from_profile(workload, n_elems):
     with open(path) as fh:
         d = json.load(fh)
     if d.get("source_hash") != source_hash() or d.get("n_elems") != n_elems:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def gemm_traffic_from_profile(m, n, k):
+    """HBM-side bytes per SR GEMM launch from the committed counter summary
+    for this shape, if it was taken on the current GEMM sources (else None)."""
+    path = os.path.join(PROFILE_DIR, f"gemm_bf16_sr_{m}x{n}x{k}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != gemm_source_hash() or d.get("shape") != [m, n, k]:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -332,7 +357,9 @@ def run_gemm(args, torch, ops, wl):
         "config": {"workload": name, "m": m, "n": n, "k": k, "layout": "C = A B^T",
                    "rounding": "sr", "accumulate": "f32"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": GEMM_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / GEMM_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / GEMM_PEAK_TFLOPS,
+                     "traffic": gemm_traffic_from_profile(m, n, k),
+                     "algorithmic_bytes": 2 * (m * k + n * k + m * n),
                      "kernel": "asr_gemm::gemm_bf16<256x256 tile, SR>",
                      "kernel_ms_avg": kernel_ms},
         "context": {"same_kernel_rn_ms": rn_ms,

@@ -1,7 +1,7 @@
 """Host logic of bench.py (CPU only): the kernel-source hash that keeps the
 committed HBM counters tied to the code they were taken on, the rule that
-`traffic` is reported only while that hash (and the element count) match,
-and the rank-share split of the Llama-3-8B list."""
+`traffic` is reported only while that hash (and the element count or GEMM
+shape) match, and the rank-share split of the Llama-3-8B list."""
 
 import json
 import os
@@ -38,6 +38,30 @@ def test_traffic_only_for_matching_code_and_size(tmp_path, monkeypatch):
     assert bench.traffic_from_profile("other", 100) is None    # no counters for it
     monkeypatch.setattr(bench, "source_hash", lambda: "def")
     assert bench.traffic_from_profile("w", 100) is None        # kernel code changed
+
+
+def test_gemm_traffic_only_for_matching_code_and_shape(tmp_path, monkeypatch):
+    doc = {"source_hash": "abc", "shape": [8, 16, 32], "hbm_bytes_per_launch": 1234.0}
+    (tmp_path / "gemm_bf16_sr_8x16x32_hbm_counters.json").write_text(json.dumps(doc))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    monkeypatch.setattr(bench, "gemm_source_hash", lambda: "abc")
+    assert bench.gemm_traffic_from_profile(8, 16, 32) == 1234.0
+    assert bench.gemm_traffic_from_profile(8, 16, 40) is None     # no counters for that shape
+    monkeypatch.setattr(bench, "gemm_source_hash", lambda: "def")
+    assert bench.gemm_traffic_from_profile(8, 16, 32) is None     # kernel code changed
+
+
+def test_committed_gemm_counters_are_consistent():
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_sr_8192x14336x4096_hbm_counters.json")
+    with open(path) as fh:
+        doc = json.load(fh)
+    m, n, k = doc["shape"]
+    assert doc["algorithmic_bytes_per_launch"] == 2 * (m * k + n * k + m * n)
+    total = doc["read_bytes_per_launch"]["sr"] + doc["write_bytes_per_launch"]["sr"]
+    assert abs(doc["hbm_bytes_per_launch"] - total) <= 2
+    # at least the output is written, and at least A and B are read
+    assert doc["write_bytes_per_launch"]["sr"] >= 2 * m * n
+    assert doc["read_bytes_per_launch"]["sr"] >= 2 * (m + n) * k
 
 
 def test_committed_counters_describe_the_llama_list():
