@@ -59,6 +59,7 @@
 #include <adamw_sr.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 #include <type_traits>
 
@@ -608,18 +609,19 @@ bool aligned_to(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
+// Compute units of the current device (cached per device, safe to call from
+// several threads; 0 if unknown).
 int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Launches one workgroup per output tile, or with `persist_grid` > 0 that
