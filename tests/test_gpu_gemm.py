@@ -237,17 +237,20 @@ def _sample_grid(extent, tile, count, rng):
     return np.array(sorted(p for p in picks if 0 <= p < extent))
 
 
-@pytest.mark.parametrize("kind", ["int", "randn"])
-def test_full_size_llama_mlp_sampled(kind):
-    """The benchmark's workload, 8192 x 14336 x 4096, in its launch
-    configuration (256 x 256 tiles, SR without the f32 copy, seed 7, base 0),
-    checked on a grid of about 72 x 72 sampled outputs. Integer operands make every
-    f32 partial sum exact (|sum| <= 4096 * 64 < 2**24), so the sampled SR and
-    RN outputs must equal the oracle's roundings of the exact products bit for
-    bit; normal operands must lie within a bf16 step of the exact product plus
-    the f32 summation bound."""
-    shape = wl.GEMM_LLAMA3_8B_MLP_UP
-    m, n, k = shape["m"], shape["n"], shape["k"]
+@pytest.mark.parametrize("kind,shape", [
+    ("int", (8192, 14336, 4096)), ("randn", (8192, 14336, 4096)),
+    ("int", (8192, 4096, 14336))], ids=["up_int", "up_randn", "down_int"])
+def test_full_size_llama_mlp_sampled(kind, shape):
+    """The benchmark's workload, 8192 x 14336 x 4096 (the gate/up projection),
+    in its launch configuration (256 x 256 tiles, persistent, SR without the
+    f32 copy, seed 7, base 0), and the down projection 8192 x 4096 x 14336
+    (224 K tiles, two tiles per workgroup), checked on a grid of about 72 x 72
+    sampled outputs. Integer operands make every f32 partial sum exact
+    (|sum| <= 14336 * 64 < 2**24), so the sampled SR and RN outputs must equal
+    the oracle's roundings of the exact products bit for bit; normal operands
+    must lie within a bf16 step of the exact product plus the f32 summation
+    bound."""
+    m, n, k = shape
     announce("gemm full size sampled", (m, n, k, kind))
     a, b = wl.gemm_operands_host(m, n, k, kind, seed=11)
     rng = np.random.default_rng(5)
