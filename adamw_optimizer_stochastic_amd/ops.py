@@ -184,6 +184,9 @@ def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, ou
     ``out_f32``: optional float32 (M x N) tensor with the same strides as
     ``out`` that also receives the unrounded result. Returns ``out``.
     """
+    if rounding not in ("rn", "sr"):
+        raise ValueError("rounding must be 'rn' or 'sr'")
+    key = (_u32("seed", seed), _u32("step", step), _u64("base_index", base_index))
     for t, name in ((a, "a"), (b, "b")):
         _require_gpu(t, name)
         if t.dtype != torch.bfloat16 or t.dim() != 2:
@@ -194,9 +197,6 @@ def gemm_bf16(a, b, *, rounding="rn", seed=0, step=0, base_index=0, out=None, ou
         raise ValueError("a and b must be on the same device")
     if a.shape[1] != b.shape[1]:
         raise ValueError(f"K mismatch: a is {tuple(a.shape)}, b is {tuple(b.shape)}")
-    if rounding not in ("rn", "sr"):
-        raise ValueError("rounding must be 'rn' or 'sr'")
-    key = (_u32("seed", seed), _u32("step", step), _u64("base_index", base_index))
     m, k = a.shape
     n = b.shape[0]
     if out is None:

@@ -47,5 +47,10 @@ def test_stream_arguments_checked_before_launch():
         ops.cvt_f32_bf16_sr(x, 0, 0, base_index=-5)
     with pytest.raises(ValueError, match="counter_base"):
         ops.philox_4x32_fill(4, -1, 0, 0)
+    ab = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="seed"):
+        ops.gemm_bf16(ab, ab, rounding="sr", seed=1 << 32)
+    with pytest.raises(ValueError, match="base_index"):
+        ops.gemm_bf16(ab, ab, rounding="sr", base_index=-1)
     with pytest.raises(ValueError, match="base_index"):
         arng._u64(1 << 64)   # the random module's position argument
