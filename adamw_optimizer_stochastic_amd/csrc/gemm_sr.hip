@@ -145,6 +145,7 @@ struct GemmArgs {
   uint32_t tiles_m, tiles_n;
   uint32_t seed, step;
   uint32_t vec_store;  // ldc % 4 == 0 and C (and c32) aligned for 8 (16) bytes
+  uint32_t vec16;      // ldc % 8 == 0 and C and c32 aligned for 16 bytes
   uint32_t pos4;       // base_index % 4 == 0 and N % 4 == 0
 };
 
@@ -261,6 +262,47 @@ __device__ __forceinline__ void store_out(const GemmArgs& args, int64_t m, int64
   }
 }
 
+// Writes output elements (m, n .. n+7), n a multiple of 8, that lie inside
+// C: with 16-byte stores when the whole run is inside and aligned, else as
+// two runs of 4.
+template <int ROUND, bool F32OUT>
+__device__ __forceinline__ void store_out8(const GemmArgs& args, int64_t m, int64_t n,
+                                           const float (&x)[8]) {
+  if (args.vec16 && n + 8 <= args.n) {
+    if constexpr (F32OUT) {
+      float* d = args.c32 + m * args.ldc + n;
+      reinterpret_cast<asr::f32x4*>(d)[0] = asr::f32x4{x[0], x[1], x[2], x[3]};
+      reinterpret_cast<asr::f32x4*>(d)[1] = asr::f32x4{x[4], x[5], x[6], x[7]};
+    }
+    const uint64_t p = args.base_index + static_cast<uint64_t>(m) * static_cast<uint64_t>(args.n) +
+                       static_cast<uint64_t>(n);
+    uint32_t r16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (ROUND == ASR_ROUND_SR) {
+      uint32_t lo[4], hi[4];
+      bits4(p, args.pos4 != 0, args.seed, args.step, lo);
+      bits4(p + 4, args.pos4 != 0, args.seed, args.step, hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r16[e] = lo[e];
+        r16[4 + e] = hi[e];
+      }
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      h[e] = ROUND == ASR_ROUND_SR ? asr::round_sr(__float_as_uint(x[e]), r16[e])
+                                   : asr::round_rn(__float_as_uint(x[e]));
+    *reinterpret_cast<asr::u32x4*>(args.c + m * args.ldc + n) =
+        asr::u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16)};
+  } else {
+    const float a[4] = {x[0], x[1], x[2], x[3]};
+    const float b[4] = {x[4], x[5], x[6], x[7]};
+    store_out<ROUND, F32OUT>(args, m, n, a);
+    if (n + 4 < args.n) store_out<ROUND, F32OUT>(args, m, n + 4, b);
+  }
+}
+
 template <typename Cfg, int ROUND, bool F32OUT, bool PERSIST>
 __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN;
@@ -342,9 +384,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 
   f32x16 acc[Cfg::kFragM][Cfg::kFragN];
   // Vector-memory instructions one wave's epilogue issues for a tile that
-  // lies wholly inside C: one 8-byte store per 4 outputs, more with the f32
-  // copy or unaligned C (never fewer).
-  constexpr int kStoresPerWave = Cfg::kFragM * Cfg::kFragN * 4;
+  // lies wholly inside C: one 16-byte store per 8 outputs (RN) or one 8-byte
+  // store per 4 (SR), more with the f32 copy or unaligned C (never fewer).
+  constexpr int kStoresPerWave = Cfg::kFragM * Cfg::kFragN * (ROUND == ASR_ROUND_RN ? 2 : 4);
   static_assert((Cfg::STAGES - 1) * Cfg::kSlabsPerWave + kStoresPerWave < 64, "vmcnt range");
 
   const uint32_t wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
@@ -533,23 +575,54 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
     return kt;
   };
   // acc[i][j] register r of lane l holds C[m][n] with m = row base + l%32
-  // and n = column base + 8*(r/4) + 4*(l/32) + r%4. Compile-time loops keep
-  // every accumulator index constant (a runtime index would move the
-  // accumulators to scratch memory).
+  // and n = column base + 8*(r/4) + 4*(l/32) + r%4: lanes l and l + 32 hold
+  // alternate runs of 4 columns of the same row. SR writes each run of 4
+  // (one Philox call, one 8-byte store). RN first makes the runs 8 long: one
+  // v_permlane32_swap per register pair (groups 2p and 2p + 1) gives lane
+  // l < 32 columns 16p .. +7 and lane l + 32 columns 16p + 8 .. +15, written
+  // with one 16-byte store (measured: RN 2-8% faster, SR 1-3% slower with
+  // the swaps, so SR keeps the runs of 4). The swaps run with every lane
+  // active, before the bounds checks. Compile-time loops keep every
+  // accumulator index constant (a runtime index would move the accumulators
+  // to scratch memory).
   auto epilogue = [&](int64_t em0, int64_t en0, uint32_t e_row, uint32_t e_half) {
+    if constexpr (ROUND != ASR_ROUND_RN) {
+      static_for<Cfg::kFragM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int64_t m = em0 + wm * Cfg::WM + i * 32 + e_row;
+        if (m >= args.m) return;
+        static_for<Cfg::kFragN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<4>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int64_t n = en0 + wn * Cfg::WN + j * 32 + 8 * q + 4 * e_half;
+            if (n >= args.n) return;
+            const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]};
+            store_out<ROUND, F32OUT>(args, m, n, x);
+          });
+        });
+      });
+      return;
+    }
     static_for<Cfg::kFragM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int64_t m = em0 + wm * Cfg::WM + i * 32 + e_row;
-      if (m >= args.m) return;
       static_for<Cfg::kFragN>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        static_for<4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          const int64_t n = en0 + wn * Cfg::WN + j * 32 + 8 * q + 4 * e_half;
-          if (n >= args.n) return;
-          const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                              acc[i][j][4 * q + 3]};
-          store_out<ROUND, F32OUT>(args, m, n, x);
+        static_for<2>([&](auto pc) {
+          constexpr int qp = decltype(pc)::value;
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(
+                __float_as_uint(acc[i][j][8 * qp + e]), __float_as_uint(acc[i][j][8 * qp + 4 + e]),
+                false, false);
+            x[e] = __uint_as_float(r[0]);
+            x[4 + e] = __uint_as_float(r[1]);
+          }
+          const int64_t n = en0 + wn * Cfg::WN + j * 32 + 16 * qp + 8 * e_half;
+          if (m < args.m && n < args.n) store_out8<ROUND, F32OUT>(args, m, n, x);
         });
       });
     });
@@ -691,6 +764,7 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb
   args.seed = seed;
   args.step = step;
   args.vec_store = ldc % 4 == 0 && aligned_to(c, 8) && (!c_f32 || aligned_to(c_f32, 16));
+  args.vec16 = ldc % 8 == 0 && aligned_to(c, 16) && (!c_f32 || aligned_to(c_f32, 16));
   args.pos4 = (base_index % 4 == 0) && (n % 4 == 0);
 
   const uint64_t big_tiles = static_cast<uint64_t>((m + 255) / 256) * ((n + 255) / 256);
