@@ -76,6 +76,11 @@ constexpr int kXcds = 8;
 #define ASR_GEMM_GROUP_M 4
 #endif
 constexpr int kGroupM = ASR_GEMM_GROUP_M;  // tile rows per group in the tile order
+// SR epilogue: 1 = lanes pair up their rounded runs into 16-byte stores,
+// 0 = each lane stores its runs of 4 (8 bytes); the results are identical.
+#ifndef ASR_GEMM_SR_SWAP
+#define ASR_GEMM_SR_SWAP 1
+#endif
 constexpr int kDmaBytes = 1024;    // LDS bytes one wave-wide 16-byte-per-lane DMA fills
 
 // Copies go through buffer resources: a resource spans kBufferRecords bytes
@@ -384,9 +389,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 
   f32x16 acc[Cfg::kFragM][Cfg::kFragN];
   // Vector-memory instructions one wave's epilogue issues for a tile that
-  // lies wholly inside C: one 16-byte store per 8 outputs (RN) or one 8-byte
-  // store per 4 (SR), more with the f32 copy or unaligned C (never fewer).
-  constexpr int kStoresPerWave = Cfg::kFragM * Cfg::kFragN * (ROUND == ASR_ROUND_RN ? 2 : 4);
+  // lies wholly inside C: one 16-byte store per 8 outputs (one 8-byte store
+  // per 4 for SR without the swap), more with the f32 copy or unaligned C
+  // (never fewer).
+  constexpr int kStoresPerWave =
+      Cfg::kFragM * Cfg::kFragN * (ROUND == ASR_ROUND_RN || ASR_GEMM_SR_SWAP ? 2 : 4);
   static_assert((Cfg::STAGES - 1) * Cfg::kSlabsPerWave + kStoresPerWave < 64, "vmcnt range");
 
   const uint32_t wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
@@ -576,16 +583,62 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
   };
   // acc[i][j] register r of lane l holds C[m][n] with m = row base + l%32
   // and n = column base + 8*(r/4) + 4*(l/32) + r%4: lanes l and l + 32 hold
-  // alternate runs of 4 columns of the same row. SR writes each run of 4
-  // (one Philox call, one 8-byte store). RN first makes the runs 8 long: one
-  // v_permlane32_swap per register pair (groups 2p and 2p + 1) gives lane
-  // l < 32 columns 16p .. +7 and lane l + 32 columns 16p + 8 .. +15, written
-  // with one 16-byte store (measured: RN 2-8% faster, SR 1-3% slower with
-  // the swaps, so SR keeps the runs of 4). The swaps run with every lane
-  // active, before the bounds checks. Compile-time loops keep every
-  // accumulator index constant (a runtime index would move the accumulators
-  // to scratch memory).
+  // alternate runs of 4 columns of the same row. v_permlane32_swap on the
+  // pair of groups 2p and 2p + 1 gives lane l < 32 columns 16p .. +7 and
+  // lane l + 32 columns 16p + 8 .. +15, written with one 16-byte store (half
+  // the store instructions of 8-byte runs). RN swaps the f32 values (4 swaps
+  // per 8 outputs); SR first rounds each lane's own runs of 4 (one Philox
+  // call each, as the keying lays them out) and swaps the packed bf16 words
+  // (2 swaps per 8 outputs; swapping the f32 values before SR measured
+  // slower). The swaps run with every lane active, before the bounds
+  // checks; runs that are ragged or unaligned fall back to 4-wide stores.
+  // Compile-time loops keep every accumulator index constant (a runtime
+  // index would move the accumulators to scratch memory).
   auto epilogue = [&](int64_t em0, int64_t en0, uint32_t e_row, uint32_t e_half) {
+    if constexpr (ROUND != ASR_ROUND_RN && ASR_GEMM_SR_SWAP) {
+      static_for<Cfg::kFragM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int64_t m = em0 + wm * Cfg::WM + i * 32 + e_row;
+        static_for<Cfg::kFragN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<2>([&](auto pc) {
+            constexpr int qp = decltype(pc)::value;
+            // this lane's own runs of 4 (groups 2qp and 2qp + 1), rounded
+            const int64_t n0q = en0 + wn * Cfg::WN + j * 32 + 16 * qp + 4 * e_half;
+            uint32_t w[2][2];
+            float xs[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xs[h][e] = acc[i][j][8 * qp + 4 * h + e];
+              uint32_t r16[4];
+              bits4(args.base_index + static_cast<uint64_t>(m) * static_cast<uint64_t>(args.n) +
+                        static_cast<uint64_t>(n0q + 8 * h),
+                    args.pos4 != 0, args.seed, args.step, r16);
+              uint32_t hb[4];
+              round4<ROUND>(xs[h], r16, hb);
+              w[h][0] = hb[0] | (hb[1] << 16);
+              w[h][1] = hb[2] | (hb[3] << 16);
+            }
+            // lane l < 32 then holds columns 16qp .. +7, lane l + 32 16qp + 8 .. +15
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+            const int64_t n8 = en0 + wn * Cfg::WN + j * 32 + 16 * qp + 8 * e_half;
+            if (m < args.m) {
+              if (args.vec16 && !F32OUT && n8 + 8 <= args.n) {
+                *reinterpret_cast<asr::u32x4*>(args.c + m * args.ldc + n8) =
+                    asr::u32x4{s0[0], s1[0], s0[1], s1[1]};
+              } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                  if (n0q + 8 * h < args.n) store_out<ROUND, F32OUT>(args, m, n0q + 8 * h, xs[h]);
+              }
+            }
+          });
+        });
+      });
+      return;
+    }
     if constexpr (ROUND != ASR_ROUND_RN) {
       static_for<Cfg::kFragM>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
