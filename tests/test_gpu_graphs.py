@@ -32,7 +32,7 @@ def test_graph_replays_match_eager():
     dev = torch.device("cuda", 0)
     announce("graph capture: inputs")
     gen = wl.device_generator(dev, wl.CFG_SMALL, 41)
-    sizes = [(1 << 20) + 77, 3000]
+    sizes = [(1 << 21) + 77, 3000]      # 2049 slots (a size class) and a table launch
     p0 = [wl.device_normal(n, 0.02, gen, dev, torch.bfloat16) for n in sizes]
     grads = [wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16) for n in sizes]
     bases = [0, sizes[0]]
