@@ -47,6 +47,10 @@
 //   * Tiles are handed to XCDs in contiguous ranges (workgroup b runs on XCD
 //     b % 8) and grouped along M inside each range, so the workgroups that
 //     share an L2 also share A and B panels.
+//   * Epilogue: lanes l and l + 32 hold alternate runs of 4 columns of one
+//     row; v_permlane32_swap pairs them into runs of 8, each written with
+//     one 16-byte store (RN swaps the f32 values; SR rounds each lane's own
+//     runs first, one Philox call per run, and swaps the packed bf16 words).
 //   * With more big tiles than CUs the launch is persistent: one workgroup
 //     per CU runs output tiles b, b + #CUs, ... (the same order), and the
 //     ring carries on across them: the next tile's first two K tiles are
