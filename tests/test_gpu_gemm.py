@@ -201,6 +201,49 @@ def test_strided_unaligned_outputs():
     assert_bits_equal(got.reshape(-1), want, "strided SR")
 
 
+@pytest.mark.parametrize("m,k,base", [(300, 72, 8), (4100, 136, 3)],
+                         ids=["small_tile", "persistent"])
+def test_aligned_stride_ragged_width(m, k, base):
+    """Rows 16-byte aligned (ldc a multiple of 8, so the epilogue pairs lanes
+    into 16-byte stores) but N = 4100 not a multiple of 8: each row's last
+    run of 8 is cut at N and falls back to 4-wide stores, and nothing past N
+    is written. The 128 x 128 tile (one workgroup per tile) and the
+    persistent 256 x 256 launch (17 x 17 tiles, two whole K tiles and a
+    partial one); a base_index that is and one that is not a multiple of 4.
+    Integer operands: RN and SR bit-exact
+    against the oracle (SR on every row of a column grid that covers each
+    tile's edges when M is large)."""
+    n, ldc = 4100, 4104
+    announce("gemm aligned stride, ragged width", (m, n, k, base))
+    a_bits, b_bits = wl.gemm_operands_host(m, n, k, "int", seed=17)
+    a, b = bf16_tensor(a_bits), bf16_tensor(b_bits)
+    exact = oracle.gemm_exact(a_bits, b_bits).astype(np.float32)
+    canary = to_host(torch.tensor([-7.0], dtype=torch.bfloat16))[0]
+    for rounding in ("rn", "sr"):
+        store = torch.full((m, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
+        c = store[:, :n]
+        ops.gemm_bf16(a, b, rounding=rounding, seed=21, step=4, base_index=base, out=c)
+        torch.cuda.synchronize()
+        h = to_host(store)
+        assert np.all(h[:, n:] == canary), rounding
+        got = np.ascontiguousarray(h[:, :n])
+        if rounding == "rn":
+            assert_bits_equal(got.reshape(-1), oracle.gemm_round(exact, "rn").reshape(-1),
+                              "RN, aligned stride")
+        elif m <= 512:
+            assert_bits_equal(got.reshape(-1),
+                              oracle.gemm_round(exact, "sr", 21, 4, base).reshape(-1),
+                              "SR, aligned stride")
+        else:
+            cols = np.array(sorted({0, 7, 8, n - 9, n - 8, n - 5, n - 4, n - 1} |
+                                   {t + d for t in range(0, n, 256) for d in (0, 7, 8, 255)
+                                    if t + d < n}))
+            rr, cc = np.meshgrid(np.arange(m), cols, indexing="ij")
+            want = oracle.gemm_round_at(exact[rr, cc].reshape(-1), rr.reshape(-1),
+                                        cc.reshape(-1), n, 21, 4, base)
+            assert_bits_equal(got[rr, cc].reshape(-1), want, "SR, aligned stride (sampled)")
+
+
 def test_f32_copy_does_not_change_the_result():
     announce("gemm with/without f32 copy")
     m, n, k = 1024, 1024, 2048
