@@ -81,7 +81,10 @@ class HostScalars:
 
 
 def host_scalars(lr, beta1, beta2, eps, weight_decay, step):
-    """The eight binary32 constants of one step (formed in binary64)."""
+    """The eight binary32 constants of one step (formed in binary64), for the
+    AdamW update torch.optim.AdamW documents ("adamw-sr" page, Usage: a
+    drop-in for it; the page prints no formula, so its documented algorithm is
+    the reading)."""
     if int(step) < 1:
         raise ValueError("step counts from 1")
     lr, beta1, beta2 = float(lr), float(beta1), float(beta2)
@@ -99,9 +102,10 @@ def host_scalars(lr, beta1, beta2, eps, weight_decay, step):
 
 
 def adamw_f32(p, g, m, v, sc):
-    """One element-wise AdamW update on float32 arrays (numpy float32 ufuncs,
-    each rounded to nearest even; numpy never fuses a multiply and an add).
-    Returns (p, m, v) as new float32 arrays."""
+    """One element-wise AdamW update on float32 arrays ("adamw-sr" page, intro
+    and Usage: decoupled-weight-decay Adam with float32 states), with numpy
+    float32 ufuncs, each rounded to nearest even (numpy never fuses a
+    multiply and an add). Returns (p, m, v) as new float32 arrays."""
     p, g, m, v = (np.asarray(x, dtype=np.float32) for x in (p, g, m, v))
     with np.errstate(all="ignore"):
         m = np.add(np.multiply(sc.b1, m), np.multiply(sc.omb1, g))
@@ -164,7 +168,9 @@ def _upcast(x, dtype):
 
 def step_tensor(param, grad, m, v, *, param_dtype, grad_dtype, base_index,
                 lr, beta1, beta2, eps, weight_decay, step, seed, rounding=ROUND_SR):
-    """One AdamW step of one tensor (numpy).
+    """One AdamW step of one tensor (numpy). ("adamw-sr" page, Method: the bf16
+    write-back draws the random bits of each element from Philox keyed by
+    (seed, step) at the element's global position base_index + i.)
 
     ``param``/``grad``: uint16 bf16 patterns when their dtype is BF16, else
     float32; ``m``/``v``: float32. Inputs are not modified.
@@ -223,8 +229,9 @@ def step_tensor_scalar(param, grad, m, v, *, param_dtype, grad_dtype, base_index
 def step_list(tensors, *, lr, beta1, beta2, eps, weight_decay, step, seed,
               rounding=ROUND_SR):
     """One step over a list of tensors, each a dict with keys param, grad, m,
-    v, param_dtype, grad_dtype, base_index. Tensors are independent; returns
-    a list of (param_new, m_new, v_new)."""
+    v, param_dtype, grad_dtype, base_index. Tensors are independent ("adamw-sr"
+    page, Correctness: pieces with their own base_index give the one-piece
+    result); returns a list of (param_new, m_new, v_new)."""
     return [step_tensor(t["param"], t["grad"], t["m"], t["v"],
                         param_dtype=t["param_dtype"], grad_dtype=t["grad_dtype"],
                         base_index=t["base_index"], lr=lr, beta1=beta1,

@@ -53,7 +53,9 @@ def _is_nan_bits(u):
 
 
 def sr_bf16(u, r16):
-    """Stochastic rounding, vectorized.
+    """Stochastic rounding, vectorized ("Add stochastic rounding and philox RNG
+    helpers", Primitives: add the random bits to the 16 dropped bits, keep the
+    high half; a NaN keeps its high half with the quiet bit set).
 
     ``u``: uint32 f32 patterns; ``r16``: random values in [0, 65536)
     (any unsigned integer array, broadcast against ``u``).
@@ -70,7 +72,8 @@ def sr_bf16(u, r16):
 
 
 def sr_bf16_scalar(u, r16):
-    """Stochastic rounding of one f32 pattern ``u`` with one 16-bit ``r16``."""
+    """Stochastic rounding of one f32 pattern ``u`` with one 16-bit ``r16``
+    (the same rule as :func:`sr_bf16`, one value at a time)."""
     u = int(u) & 0xFFFFFFFF
     r16 = int(r16)
     if not 0 <= r16 <= 0xFFFF:
@@ -81,7 +84,8 @@ def sr_bf16_scalar(u, r16):
 
 
 def rn_bf16(u):
-    """Round to nearest, ties to even, vectorized: uint32 patterns -> uint16."""
+    """Round to nearest, ties to even, vectorized: uint32 patterns -> uint16
+    (the comparison mode, "rn", of the FlyDSL pull request's Consumer section)."""
     u = np.asarray(u, dtype=np.uint32).astype(np.uint64)
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)

@@ -15,12 +15,16 @@ from .stream import random16
 
 
 def cvt_f32_bf16_sr(x, seed, step, base_index=0):
-    """float32 array -> uint16 bf16 patterns by stochastic rounding."""
+    """float32 array -> uint16 bf16 patterns by stochastic rounding ("Add
+    stochastic rounding and philox RNG helpers", discussion: SR as a rounding
+    mode of the conversion; element i takes the bits of position base_index + i
+    under (seed, step), the keying of the "adamw-sr" page's Method section)."""
     bits = f32_bits(np.asarray(x, dtype=np.float32).reshape(-1))
     pos = np.uint64(int(base_index) & 0xFFFFFFFFFFFFFFFF) + np.arange(bits.size, dtype=np.uint64)
     return sr_bf16(bits, random16(pos, seed, step))
 
 
 def cvt_f32_bf16_rn(x):
-    """float32 array -> uint16 bf16 patterns, round to nearest even."""
+    """float32 array -> uint16 bf16 patterns, round to nearest even (the
+    conversion's default mode in the same discussion)."""
     return rn_bf16(f32_bits(np.asarray(x, dtype=np.float32).reshape(-1)))

@@ -84,7 +84,10 @@ def f32_sum_bound(a_bits, b_bits):
 
 def gemm_round(c_f32, rounding, seed=0, step=0, base_index=0):
     """bf16 patterns of an M x N f32 result: "rn" or "sr" (position
-    base_index + m*N + n, key (seed, step))."""
+    base_index + m*N + n, key (seed, step)). "Add stochastic rounding and
+    philox RNG helpers", GEMM section: the f32 accumulator goes to bf16 by SR
+    keyed per output element, RN by default; reading: the position is the
+    row-major index."""
     c = np.asarray(c_f32, dtype=np.float32)
     bits = f32_bits(c.reshape(-1))
     if rounding == "rn":
@@ -99,7 +102,7 @@ def gemm_round(c_f32, rounding, seed=0, step=0, base_index=0):
 
 
 def gemm_round_at(c_f32_values, rows, cols, n_cols, seed, step, base_index=0):
-    """SR patterns of selected elements: c_f32_values[i] is output element
+    """SR patterns of selected elements (the rule of :func:`gemm_round`): c_f32_values[i] is output element
     (rows[i], cols[i]) of a result with n_cols columns."""
     bits = f32_bits(np.asarray(c_f32_values, dtype=np.float32).reshape(-1))
     pos = (np.uint64(int(base_index) & 0xFFFFFFFFFFFFFFFF)

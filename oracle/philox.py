@@ -31,7 +31,9 @@ _M32 = 0xFFFFFFFF
 
 
 def philox4x32_10_scalar(ctr, key, rounds=ROUNDS):
-    """Pure-Python Philox4x32 on one counter.
+    """Pure-Python Philox4x32 on one counter (the generator the FlyDSL pull
+    request's Primitives section names; constants and rounds from Salmon et
+    al., SC 2011).
 
     ``ctr``: 4 ints (each taken modulo 2**32); ``key``: 2 ints.
     Returns a tuple of 4 ints in [0, 2**32).
@@ -51,7 +53,8 @@ def philox4x32_10_scalar(ctr, key, rounds=ROUNDS):
 
 
 def philox4x32_10(c0, c1, c2, c3, k0, k1, rounds=ROUNDS):
-    """Vectorized Philox4x32 (numpy).
+    """Vectorized Philox4x32 (numpy), the same generator as
+    :func:`philox4x32_10_scalar`.
 
     Counter words and key words broadcast against each other; each is
     converted to uint32 (values must lie in [0, 2**32)). The 32x32->64

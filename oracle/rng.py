@@ -44,7 +44,9 @@ TWO_M24 = np.float32(2.0 ** -24)
 
 def words(positions, seed, step):
     """The 32-bit stream word of every position (uint32), one Philox call
-    per position."""
+    per position (FlyDSL pull request, discussion: the counter-based
+    generator also serves dropout and initialisation; the keying is the
+    "adamw-sr" page's Method: key (seed, step), call p >> 2, word p & 3)."""
     p = np.asarray(positions, dtype=np.uint64)
     j = p >> np.uint64(2)
     w = (p & np.uint64(3)).astype(np.intp)
@@ -59,11 +61,14 @@ def _positions(n, base_index):
 
 
 def unit_from_word(w):
-    """(W >> 8) * 2**-24 in binary32 (exact)."""
+    """(W >> 8) * 2**-24 in binary32 (exact): the uniform draw of a word in
+    [0, 1) (reading: the top 24 bits, so the value is exact in binary32)."""
     return (np.asarray(w, dtype=np.uint32) >> np.uint32(8)).astype(np.float32) * TWO_M24
 
 
 def uniform_f32(n, seed, step, base_index=0, low=0.0, high=1.0):
+    """Uniform draws in [low, high) for initialisation (FlyDSL pull request,
+    discussion): f32(low) + f32(high - low) * U, each step rounded in binary32."""
     u = unit_from_word(words(_positions(n, base_index), seed, step))
     width = np.float32(float(high) - float(low))   # rounded once
     return (np.float32(low) + (width * u).astype(np.float32)).astype(np.float32)
@@ -93,17 +98,21 @@ def normal_f64(n, seed, step, base_index=0, mean=0.0, std=1.0):
 
 
 def dropout_threshold(p):
+    """floor(p * 2**32): an element is dropped when its word is below it
+    (dropout, FlyDSL pull request discussion), so P(drop) = threshold / 2**32."""
     if not (0.0 <= p < 1.0):
         raise ValueError("p must be in [0, 1)")
     return min(math.floor(p * 2.0 ** 32), _M32)
 
 
 def dropout_scale(p):
+    """The scale of kept elements, 1 / (1 - p) rounded once to binary32."""
     return np.float32(1.0 / (1.0 - p))
 
 
 def dropout_keep(n, p, seed, step, base_index=0):
-    """Boolean keep mask."""
+    """Boolean keep mask: the word of position base_index + i is at or above
+    the drop threshold."""
     return words(_positions(n, base_index), seed, step) >= np.uint32(dropout_threshold(p))
 
 

@@ -25,7 +25,10 @@ _M32 = 0xFFFFFFFF
 
 
 def random16_scalar(position, seed, step):
-    """The 16-bit random value of one global position (pure Python)."""
+    """The 16-bit random value of one global position (pure Python):
+    "adamw-sr" page, Method (key (seed, step), indexed by global position);
+    the four words of one call serve four consecutive positions and each
+    position takes the low 16 bits of its word."""
     p = int(position) & 0xFFFFFFFFFFFFFFFF
     j = p >> 2
     words = philox4x32_10_scalar((j & _M32, j >> 32, 0, 0),
@@ -34,7 +37,8 @@ def random16_scalar(position, seed, step):
 
 
 def random16(positions, seed, step):
-    """The 16-bit random values of an array of global positions (numpy).
+    """The 16-bit random values of an array of global positions (numpy), by
+    the rule of :func:`random16_scalar`.
 
     ``positions``: uint64-convertible array. Returns uint32 values < 65536.
     Each element runs its own Philox call (no sharing between neighbours),
@@ -51,7 +55,8 @@ def random16(positions, seed, step):
 
 
 def philox_fill(n_counters, counter_base, seed, step, counter_upper=0):
-    """The words of ``n_counters`` consecutive Philox calls, flattened.
+    """The words of ``n_counters`` consecutive Philox calls, flattened (the raw
+    word primitive of the FlyDSL pull request's Primitives section).
 
     Call k uses counter (lo32(c), hi32(c), lo32(counter_upper),
     hi32(counter_upper)) with c = (counter_base + k) mod 2**64 and key
