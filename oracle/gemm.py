@@ -102,8 +102,9 @@ def gemm_round(c_f32, rounding, seed=0, step=0, base_index=0):
 
 
 def gemm_round_at(c_f32_values, rows, cols, n_cols, seed, step, base_index=0):
-    """SR patterns of selected elements (the rule of :func:`gemm_round`): c_f32_values[i] is output element
-    (rows[i], cols[i]) of a result with n_cols columns."""
+    """SR patterns of selected elements (the rule of :func:`gemm_round`):
+    c_f32_values[i] is output element (rows[i], cols[i]) of a result with
+    n_cols columns."""
     bits = f32_bits(np.asarray(c_f32_values, dtype=np.float32).reshape(-1))
     pos = (np.uint64(int(base_index) & 0xFFFFFFFFFFFFFFFF)
            + np.asarray(rows, dtype=np.uint64) * np.uint64(n_cols)
