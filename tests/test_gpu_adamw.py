@@ -450,6 +450,65 @@ def test_degenerate_hyperparameters(hp):
             assert_bits_equal(to_host(pd), p, "lr = 0 keeps the parameters")
 
 
+def test_thousands_of_tensors_and_more_size_classes_than_launches():
+    """One call over 3,000 tiny tensors (1..599 elements, many sizes
+    repeated) and 66 pairs of equal-size tensors of about 2**20 elements.
+    Each pair fills 2,050 or more 1,024-element slots, enough for a launch
+    of its own, but the library gives at most 64 sizes one per dtype pair:
+    the two largest pairs share the slot-table launch with the tiny
+    tensors. Tiny tensors are checked in full, the large ones on windows at
+    the start, the middle and the end, all bit for bit against the oracle."""
+    dev = torch.device("cuda", 0)
+    rng = wl.host_rng(wl.CFG_SMALL, 91, 0)
+    gen = wl.device_generator(dev, wl.CFG_SMALL, 91, 0)
+    tiny_sizes = [int(x) for x in rng.integers(1, 600, 3000)]
+    big_sizes = [(1 << 20) + 1 + 37 * c for c in range(66) for _ in range(2)]
+    assert len(set(big_sizes)) == 66 and all((n + 1023) // 1024 * 2 >= 2048 for n in big_sizes)
+    announce("3000 tiny + 66 size classes: inputs")
+    host, dev_t, bases, base = [], [], [], 11
+    for n in tiny_sizes:
+        p = _host_tensor(rng, n, BF16, 0.02)
+        g = _host_tensor(rng, n, BF16, 1e-3)
+        m = wl.normal_f32(rng, n, 1e-4)
+        v = np.abs(wl.normal_f32(rng, n, 1e-7))
+        host.append(("tiny", (p, g, m, v), base))
+        dev_t.append((bf16_tensor(p), bf16_tensor(g), f32_tensor(m), f32_tensor(v)))
+        bases.append(base)
+        base += n + 5
+    win = 2048
+    for n in big_sizes:
+        p = wl.device_normal(n, 0.02, gen, dev, torch.bfloat16)
+        g = wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16)
+        m = wl.device_normal(n, 1e-4, gen, dev, torch.float32)
+        v = wl.device_normal(n, 1e-7, gen, dev, torch.float32).abs_()
+        windows = []
+        for s in (0, n // 2 - win // 2 + 1, n - win):
+            sl = slice(s, s + win)
+            windows.append((s, to_host(p[sl]), to_host(g[sl]), to_host(m[sl]), to_host(v[sl])))
+        host.append(("big", windows, base))
+        dev_t.append((p, g, m, v))
+        bases.append(base)
+        base += n + 3
+    announce("3000 tiny + 66 size classes: step")
+    ops.adamw_step([d[0] for d in dev_t], [d[1] for d in dev_t], [d[2] for d in dev_t],
+                   [d[3] for d in dev_t], bases, step=3, seed=21, **HP)
+    torch.cuda.synchronize()
+    announce("3000 tiny + 66 size classes: oracle")
+    for k, ((kind, data, b), d) in enumerate(zip(host, dev_t)):
+        if kind == "tiny":
+            p, g, m, v = data
+            want = oracle.step_tensor(p, g, m, v, param_dtype=BF16, grad_dtype=BF16,
+                                      base_index=b, step=3, seed=21, **HP)
+            _check_outputs((d[0], d[2], d[3]), want, BF16, f"tiny tensor {k} (n={p.size})")
+            continue
+        for s, p, g, m, v in data:
+            want = oracle.step_tensor(p, g, m, v, param_dtype=BF16, grad_dtype=BF16,
+                                      base_index=b + s, step=3, seed=21, **HP)
+            sl = slice(s, s + win)
+            _check_outputs((d[0][sl], d[2][sl], d[3][sl]), want, BF16,
+                           f"tensor {k} (n={d[0].numel()}) window {s}")
+
+
 def test_overlapping_buffers_are_rejected():
     """p, m and v are written in place, so the binding refuses buffers that
     share memory (here: one tensor's exp_avg_sq is a view into another's
