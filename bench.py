@@ -43,6 +43,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f
                   for f in ("adamw_sr.hip", "device.hpp")]
 GEMM_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f)
                 for f in ("gemm_sr.hip", "device.hpp")]
+RNG_SOURCES = [os.path.join(ROOT, "adamw_optimizer_stochastic_amd", "csrc", f)
+               for f in ("random.hip", "device.hpp")]
 
 
 def source_hash_of(files):
@@ -66,6 +68,11 @@ def source_hash():
 def gemm_source_hash():
     """Hash of the GEMM's kernel sources (see source_hash_of)."""
     return source_hash_of(GEMM_SOURCES)
+
+
+def rng_source_hash():
+    """Hash of the random fills' and dropout's kernel sources (see source_hash_of)."""
+    return source_hash_of(RNG_SOURCES)
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -118,6 +125,20 @@ def traffic_from_profile(workload, n_elems):
     with open(path) as fh:
         d = json.load(fh)
     if d.get("source_hash") != source_hash() or d.get("n_elems") != n_elems:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def stream_traffic_from_profile(name, source_hash_now, n_elems):
+    """HBM bytes per launch of a single-kernel streaming workload (the
+    conversion, dropout) from its committed counter summary, if it was taken
+    on the current kernel sources at this size (else None)."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != source_hash_now or d.get("n_elems") != n_elems:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -240,8 +261,10 @@ def run_convert(args, torch, ops, wl):
             "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
             "config": {"workload": "cvt_f32_bf16_sr_2^30"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel_ms_avg": kernel_ms}}
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": stream_traffic_from_profile(
+                             "cvt_f32_bf16_sr_2pow30_hbm_counters.json", source_hash(), n),
+                         "algorithmic_bytes": 6 * n, "kernel_ms_avg": kernel_ms}}
 
 
 GEMM_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
@@ -409,7 +432,10 @@ def run_rng(args, torch, ops, wl):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "dropout_2^30_f32_p0.1", "algorithmic_bytes_per_element": 9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stream_traffic_from_profile(
+                         "rng_dropout_2pow30_hbm_counters.json", rng_source_hash(), n),
+                     "algorithmic_bytes": 9 * n,
                      "kernel": "asr_rng::rng_kernel<dropout, f32>", "kernel_ms_avg": drop_ms},
         "context": {"normal_fill_ms": normal_ms,
                     "normal_fill_GBps": 4 * n / (normal_ms * 1e-3) / 1e9,

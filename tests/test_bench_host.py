@@ -7,6 +7,8 @@ import json
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
@@ -71,6 +73,30 @@ def test_committed_counters_describe_the_llama_list():
     assert doc["n_elems"] == 8030261248
     # scaled counter bytes equal the algorithmic 22 B/element to within 0.1%
     assert abs(doc["hbm_bytes_per_launch"] / (22 * doc["n_elems"]) - 1) < 1e-3
+
+
+@pytest.mark.parametrize("name,hash_fn,per_elem", [
+    ("cvt_f32_bf16_sr_2pow30_hbm_counters.json", "source_hash", 6),
+    ("rng_dropout_2pow30_hbm_counters.json", "rng_source_hash", 9)])
+def test_committed_streaming_counters_are_current_and_reported(name, hash_fn, per_elem):
+    """The conversion's and dropout's counter summaries were taken on the
+    current sources, their scaled bytes match the algorithmic ones to within
+    0.1%, and the benchmark reports them; a stale hash or another size gives
+    None."""
+    import bench
+    path = os.path.join(ROOT, "profiles", name)
+    with open(path) as fh:
+        doc = json.load(fh)
+    n = doc["n_elems"]
+    assert doc["algorithmic_bytes_per_launch"] == per_elem * n
+    assert abs(doc["hbm_bytes_per_launch"] / (per_elem * n) - 1) < 1e-3
+    assert abs(doc["read_bytes_per_launch"] + doc["write_bytes_per_launch"]
+               - doc["hbm_bytes_per_launch"]) <= 2
+    now = getattr(bench, hash_fn)()
+    assert doc["source_hash"] == now
+    assert bench.stream_traffic_from_profile(name, now, n) == doc["hbm_bytes_per_launch"]
+    assert bench.stream_traffic_from_profile(name, "0" * 16, n) is None
+    assert bench.stream_traffic_from_profile(name, now, n + 1) is None
 
 
 def test_rank_pieces_partition_the_list():
