@@ -50,10 +50,12 @@ def _run(a_bits, b_bits, rounding, seed=0, step=0, base=0, f32=True):
 
 
 # (M, N, K): single elements, one partial tile, several 128-tiles with
-# ragged edges, K not a multiple of 64, and the 256-tile path (>= 256 tiles)
-# with ragged M and N.
+# ragged edges, K not a multiple of 64, the 128-tile in 4 waves (more
+# 128-tiles than CUs, fewer than 256 256-tiles) and the 256-tile path
+# (>= 256 tiles) with ragged M and N. The other small shapes have no more
+# 128-tiles than CUs and run the 128-tile in 8 waves.
 SHAPES = [(1, 1, 8), (5, 3, 16), (33, 65, 72), (128, 128, 64), (130, 257, 200),
-          (256, 512, 1024), (4100, 4097, 136)]
+          (256, 512, 1024), (2000, 2100, 72), (4100, 4097, 136)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
