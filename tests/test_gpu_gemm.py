@@ -49,13 +49,14 @@ def _run(a_bits, b_bits, rounding, seed=0, step=0, base=0, f32=True):
     return to_host(c), (to_host(c32) if f32 else None)
 
 
-# (M, N, K): single elements, one partial tile, several 128-tiles with
-# ragged edges, K not a multiple of 64, the 128-tile in 4 waves (more
-# 128-tiles than CUs, fewer than 256 256-tiles) and the 256-tile path
-# (>= 256 tiles) with ragged M and N. The other small shapes have no more
-# 128-tiles than CUs and run the 128-tile in 8 waves.
+# (M, N, K): single elements, one partial tile, several tiles with ragged
+# edges, K not a multiple of 64, and one shape per tile configuration: up to
+# a quarter as many 128-tiles as CUs run the 64 x 64 tile (the first six
+# shapes), up to one 128-tile per CU the 128-tile in 8 waves (1100 x 1500),
+# more the 128-tile in 4 waves (2000 x 2100), and 256 or more 256-tiles
+# the 256-tile path with ragged M and N (4100 x 4097).
 SHAPES = [(1, 1, 8), (5, 3, 16), (33, 65, 72), (128, 128, 64), (130, 257, 200),
-          (256, 512, 1024), (2000, 2100, 72), (4100, 4097, 136)]
+          (256, 512, 1024), (1100, 1500, 136), (2000, 2100, 72), (4100, 4097, 136)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
