@@ -61,7 +61,9 @@
 //     64 x 32 when there are no more such tiles than CUs, else 4 waves of
 //     64 x 64 (two workgroups to a CU). With at most a quarter as many
 //     128 x 128 tiles as CUs, a 64 x 64 tile in 4 waves of 32 x 32 gives
-//     four times as many workgroups.
+//     four times as many workgroups. Where a CU runs a single workgroup
+//     (the 8-wave 128 x 128 tile, the 64 x 64 tile) the ring is 3 and 4
+//     K tiles deep: such grids are latency-bound, and the LDS is free.
 #include "device.hpp"
 #include "status.hpp"
 
@@ -726,10 +728,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 #define ASR_GEMM_SMALL 128, 128, 64, 64, 64, 2
 #endif
 #ifndef ASR_GEMM_SMALL8
-#define ASR_GEMM_SMALL8 128, 128, 64, 32, 64, 2
+#define ASR_GEMM_SMALL8 128, 128, 64, 32, 64, 3
 #endif
 #ifndef ASR_GEMM_TINY
-#define ASR_GEMM_TINY 64, 64, 32, 32, 64, 2
+#define ASR_GEMM_TINY 64, 64, 32, 32, 64, 4
 #endif
 #ifndef ASR_GEMM_PERSIST
 #define ASR_GEMM_PERSIST 1
