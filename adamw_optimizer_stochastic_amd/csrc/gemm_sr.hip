@@ -59,7 +59,7 @@
 //     in flight (vector-memory operations complete in issue order).
 //   * Grids of fewer than 256 big tiles use a 128 x 128 tile: 8 waves of
 //     64 x 32 when there are no more such tiles than CUs, else 4 waves of
-//     64 x 64 (two workgroups to a CU). With at most a quarter as many
+//     64 x 64 (two workgroups to a CU). With at most half as many
 //     128 x 128 tiles as CUs, a 64 x 64 tile in 4 waves of 32 x 32 gives
 //     four times as many workgroups. Where a CU runs a single workgroup
 //     (the 8-wave 128 x 128 tile, the 64 x 64 tile) the ring is 3 and 4
@@ -742,10 +742,13 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
 #ifndef ASR_GEMM_USE_TINY
 #define ASR_GEMM_USE_TINY 1
 #endif
+#ifndef ASR_GEMM_TINY_DIV
+#define ASR_GEMM_TINY_DIV 2
+#endif
 using Big = TileCfg<ASR_GEMM_BIG>;        // 8 waves, 2 per SIMD
 using Small = TileCfg<ASR_GEMM_SMALL>;    // 4 waves, for grids too small for Big
 using Small8 = TileCfg<ASR_GEMM_SMALL8>;  // the same tile in 8 waves, for at most one tile per CU
-using Tiny = TileCfg<ASR_GEMM_TINY>;      // 4 waves of 32 x 32, for grids of a quarter as many tiles as CUs
+using Tiny = TileCfg<ASR_GEMM_TINY>;      // 4 waves of 32 x 32, for grids of up to half as many tiles as CUs
 
 }  // namespace asr_gemm
 
@@ -860,7 +863,7 @@ int asr_gemm_bf16(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb
   // workgroup, so the tile runs as 8 waves (two per SIMD, one hiding the
   // other's latency); with more tiles, 4-wave workgroups share the CUs.
   const bool small8 = ASR_GEMM_SMALL_WAVES8 && cus > 0 && small_tiles <= static_cast<uint64_t>(cus);
-  const bool tiny = ASR_GEMM_USE_TINY && cus > 0 && small_tiles * 4 <= static_cast<uint64_t>(cus);
+  const bool tiny = ASR_GEMM_USE_TINY && cus > 0 && small_tiles * ASR_GEMM_TINY_DIV <= static_cast<uint64_t>(cus);
   hipError_t e;
   if (big_tiles < 256 && tiny) e = dispatch<asr_gemm::Tiny, false>(args, rounding, 0, s);
   else if (big_tiles < 256 && small8) e = dispatch<asr_gemm::Small8, false>(args, rounding, 0, s);

@@ -51,12 +51,12 @@ def _run(a_bits, b_bits, rounding, seed=0, step=0, base=0, f32=True):
 
 # (M, N, K): single elements, one partial tile, several tiles with ragged
 # edges, K not a multiple of 64, and one shape per tile configuration: up to
-# a quarter as many 128-tiles as CUs run the 64 x 64 tile (the first six
-# shapes), up to one 128-tile per CU the 128-tile in 8 waves (1100 x 1500),
+# half as many 128-tiles as CUs run the 64 x 64 tile (the first six
+# shapes), up to one 128-tile per CU the 128-tile in 8 waves (1700 x 1500),
 # more the 128-tile in 4 waves (2000 x 2100), and 256 or more 256-tiles
 # the 256-tile path with ragged M and N (4100 x 4097).
 SHAPES = [(1, 1, 8), (5, 3, 16), (33, 65, 72), (128, 128, 64), (130, 257, 200),
-          (256, 512, 1024), (1100, 1500, 136), (2000, 2100, 72), (4100, 4097, 136)]
+          (256, 512, 1024), (1700, 1500, 136), (2000, 2100, 72), (4100, 4097, 136)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -210,7 +210,7 @@ def test_aligned_stride_ragged_width(m, k, base):
     """Rows 16-byte aligned (ldc a multiple of 8, so the epilogue pairs lanes
     into 16-byte stores) but N = 4100 not a multiple of 8: each row's last
     run of 8 is cut at N and falls back to 4-wide stores, and nothing past N
-    is written. The 128 x 128 tile (one workgroup per tile) and the
+    is written. The 64 x 64 tile (one workgroup per tile) and the
     persistent 256 x 256 launch (17 x 17 tiles, two whole K tiles and a
     partial one); a base_index that is and one that is not a multiple of 4.
     Integer operands: RN and SR bit-exact
