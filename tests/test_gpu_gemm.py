@@ -176,6 +176,30 @@ def test_row_block_alone_reproduces_rows():
     assert np.array_equal(part, whole[r0:r1])
 
 
+def test_result_independent_of_tile_configuration():
+    """Normal operands, N = 4096, K = 264: the first M rows of A for M =
+    4352 (256-tile, persistent), 4096 (256-tile, one workgroup per tile),
+    2048 (128-tile, 4 waves), 768 (128-tile, 8 waves) and 256 (64-tile).
+    Every configuration accumulates each output's K in the same order, so
+    the f32 results and the SR outputs of the shared rows are identical
+    bit for bit; the f32 results also stay within the oracle's bound."""
+    n, k = 4096, 264
+    a_bits, b_bits = wl.gemm_operands_host(4352, n, k, "randn", seed=8)
+    seed, step, base = 3, 5, 11
+    announce("gemm tile configurations: M = 4352")
+    whole, whole32 = _run(a_bits, b_bits, "sr", seed, step, base)
+    rows = np.r_[0:40, 700:730, 2040:2048, 4090:4096, 4312:4352]
+    exact = np.stack([[oracle.gemm_dot(a_bits[r], b_bits[c]) for c in range(0, n, 97)]
+                      for r in rows])
+    bound = oracle.f32_sum_bound(a_bits[rows], b_bits[::97])
+    assert np.all(np.abs(whole32[rows][:, ::97].astype(np.float64) - exact) <= bound)
+    for m in (4096, 2048, 768, 256):
+        announce("gemm tile configurations: M =", m)
+        part, part32 = _run(a_bits[:m], b_bits, "sr", seed, step, base)
+        assert_bits_equal(part32.reshape(-1), whole32[:m].reshape(-1), f"f32 result, M = {m}")
+        assert_bits_equal(part.reshape(-1), whole[:m].reshape(-1), f"SR output, M = {m}")
+
+
 def test_strided_unaligned_outputs():
     announce("gemm strided/unaligned")
     m, n, k = 97, 203, 48   # N odd: no 4-element groups, positions unaligned
