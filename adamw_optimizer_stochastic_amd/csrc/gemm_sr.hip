@@ -3,7 +3,7 @@
 //
 // Sources (pages cited by title and section):
 //   "Add stochastic rounding and philox RNG helpers" (FlyDSL pull request):
-//     GEMM section (a bf16 GEMM whose f32 accumulator goes to bf16 by SR
+//     Consumer section (a bf16 GEMM whose f32 accumulator goes to bf16 by SR
 //     instead of RN, the random bits keyed per output element from a seed;
 //     RN stays the default) and Tests (SR stays within tolerance of RN,
 //     changes with the seed, reproducible for a fixed seed).
@@ -634,9 +634,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16(GemmArgs args) {
             // lane l < 32 then holds columns 16qp .. +7, lane l + 32 16qp + 8 .. +15
             const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-            const int64_t n8 = en0 + wn * Cfg::WN + j * 32 + 16 * qp + 8 * e_half;
+            // Both lanes of the pair must take the same branch: the 16-byte
+            // stores write the partner's run too, so they are taken only when
+            // all 16 columns of the pair are inside the row; otherwise each
+            // lane writes its own two runs.
+            const int64_t n16 = en0 + wn * Cfg::WN + j * 32 + 16 * qp;
+            const int64_t n8 = n16 + 8 * e_half;
             if (m < args.m) {
-              if (args.vec16 && !F32OUT && n8 + 8 <= args.n) {
+              if (args.vec16 && !F32OUT && n16 + 16 <= args.n) {
                 *reinterpret_cast<asr::u32x4*>(args.c + m * args.ldc + n8) =
                     asr::u32x4{s0[0], s1[0], s0[1], s1[1]};
               } else {

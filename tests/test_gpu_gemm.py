@@ -271,6 +271,45 @@ def test_aligned_stride_ragged_width(m, k, base):
             assert_bits_equal(got[rr, cc].reshape(-1), want, "SR, aligned stride (sampled)")
 
 
+@pytest.mark.parametrize("n", [4105, 4109, 4111])
+@pytest.mark.parametrize("m", [300, 700, 2000, 4100],
+                         ids=["tile64", "tile128_8waves", "tile128_4waves", "persistent"])
+def test_aligned_stride_width_9_to_15_past_16(m, n):
+    """Rows 16-byte aligned (ldc = 4112) with N mod 16 in 9..15: in each
+    row's last group of 16 columns, the first lane of a pair has its 8
+    columns inside the row and its partner does not. The SR epilogue pairs
+    lanes into 16-byte stores only when all 16 columns are inside, so every
+    column up to N is written (by the pair or by each lane's own 4-wide
+    runs) and nothing past N is. Every tile configuration: the 64 x 64 tile,
+    the 128 x 128 tile in 8 and in 4 waves, and the persistent 256 x 256
+    launch. Integer operands: RN and SR bit-exact against the oracle, SR on
+    every row at the last 40 columns and at each 16-column group's edges."""
+    ldc, k, base = 4112, 136, 5
+    announce("gemm ragged 16-byte pairs", (m, n, k))
+    a_bits, b_bits = wl.gemm_operands_host(m, n, k, "int", seed=23)
+    a, b = bf16_tensor(a_bits), bf16_tensor(b_bits)
+    exact = oracle.gemm_exact(a_bits, b_bits).astype(np.float32)
+    canary = to_host(torch.tensor([-7.0], dtype=torch.bfloat16))[0]
+    cols = np.array(sorted(set(range(n - 40, n)) |
+                           {t + d for t in range(0, n, 16) for d in (0, 7, 8, 15) if t + d < n}))
+    rr, cc = np.meshgrid(np.arange(m), cols, indexing="ij")
+    for rounding in ("rn", "sr"):
+        store = torch.full((m, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
+        c = store[:, :n]
+        ops.gemm_bf16(a, b, rounding=rounding, seed=3, step=9, base_index=base, out=c)
+        torch.cuda.synchronize()
+        h = to_host(store)
+        assert np.all(h[:, n:] == canary), (rounding, "written past N")
+        got = np.ascontiguousarray(h[:, :n])
+        if rounding == "rn":
+            assert_bits_equal(got.reshape(-1), oracle.gemm_round(exact, "rn").reshape(-1),
+                              "RN, ragged 16-byte pairs")
+        else:
+            want = oracle.gemm_round_at(exact[rr, cc].reshape(-1), rr.reshape(-1),
+                                        cc.reshape(-1), n, 3, 9, base)
+            assert_bits_equal(got[rr, cc].reshape(-1), want, "SR, ragged 16-byte pairs")
+
+
 def test_f32_copy_does_not_change_the_result():
     announce("gemm with/without f32 copy")
     m, n, k = 1024, 1024, 2048
