@@ -18,6 +18,16 @@ import torch
 from . import ops
 
 
+def _step_count(x):
+    """A saved step count as a Python int: from an int, or from a tensor of
+    any dtype (torch's own AdamW saves a float32 tensor)."""
+    if isinstance(x, torch.Tensor):
+        x = x.item()
+    if float(x) != int(x) or int(x) < 0:
+        raise ValueError(f"step count must be a non-negative integer (got {x})")
+    return int(x)
+
+
 class AdamWSR(torch.optim.Optimizer):
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=1e-2,
                  *, seed=0, rounding="sr", amsgrad=False, maximize=False, foreach=None,
@@ -99,7 +109,9 @@ class AdamWSR(torch.optim.Optimizer):
                     raise NotImplementedError("AdamWSR needs contiguous params and grads")
                 state = self.state[p]
                 if len(state) == 0:
-                    state["step"] = torch.tensor(0.0, dtype=torch.float32)
+                    # int64, not torch's float32: a float32 count stops at 2**24,
+                    # and from there every step would reuse one key (seed, step)
+                    state["step"] = torch.tensor(0, dtype=torch.int64)
                     state["exp_avg"] = torch.zeros_like(p, dtype=torch.float32,
                                                         memory_format=torch.contiguous_format)
                     state["exp_avg_sq"] = torch.zeros_like(p, dtype=torch.float32,
@@ -140,7 +152,7 @@ class AdamWSR(torch.optim.Optimizer):
             if st is None:
                 continue
             self.state[p] = {
-                "step": torch.as_tensor(st["step"], dtype=torch.float32).detach().clone().cpu(),
+                "step": torch.tensor(_step_count(st["step"]), dtype=torch.int64),
                 "exp_avg": st["exp_avg"].detach().to(device=p.device, dtype=torch.float32).clone(),
                 "exp_avg_sq": st["exp_avg_sq"].detach().to(device=p.device,
                                                             dtype=torch.float32).clone(),

@@ -124,8 +124,14 @@ size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors);
  * of range, rounding code unknown, more than 2**32 slots of 1,024 elements
  * of one dtype pair), ASR_EDTYPE, ASR_EALIGN (param/grad not aligned to 2 or 4 bytes as
  * their dtype needs, m/v not 4-byte aligned), ASR_EWORKSPACE, ASR_EHIP.
- * Tensors whose four buffers are 16-byte aligned take the 128-bit path;
- * others are processed element by element with identical results.
+ * Layout of the work: each tensor is walked in runs of 4 consecutive
+ * elements, one run per GPU lane, shifted by s elements (0 <= s < 4) so
+ * that every whole run starts on a vector-aligned address of all four
+ * buffers (16 bytes for f32, 8 for bf16) -- a tensor cut out of aligned
+ * buffers at any element offset has such a shift. Whole runs move with
+ * vector accesses; the cut runs at either end, and every run of a tensor
+ * whose buffers are misaligned against each other (no such shift), move
+ * element by element. The results are the same either way.
  */
 int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors,
                    double lr, double beta1, double beta2, double eps,
@@ -194,7 +200,7 @@ int asr_sr_bf16_given_bits(const float* x, const uint16_t* r16, uint16_t* out,
 
 /*
  * bf16 GEMM with a stochastic-rounding (or round-to-nearest) epilogue.
- * ("Add stochastic rounding and philox RNG helpers", GEMM section: the f32
+ * ("Add stochastic rounding and philox RNG helpers", Consumer section: the f32
  * accumulator of a bf16 GEMM is converted to bf16 by SR keyed per output
  * element from a seed, RN being the other rounding; Tests: SR within
  * tolerance of RN, seed-dependent, reproducible.)
@@ -287,6 +293,39 @@ int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype,
 int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
 /*
+ * Measurement support: what HBM gives a plain stream under the launch
+ * structure of asr_stream_copy (16 KiB slot per workgroup, 128-bit
+ * accesses, XCD windows, residency cap). The benchmark reports these
+ * beside the AdamW step as the memory ceiling it is measured against.
+ *   ASR_PROBE_READ   reads `bytes` bytes of src. Fill src with equal 16-byte
+ *                    words (e.g. all bytes alike): the kernel then writes
+ *                    nothing; dst is a 16-byte sink that it could write
+ *                    otherwise.
+ *   ASR_PROBE_WRITE  writes `bytes` bytes of dst (src unused, may be NULL).
+ *   ASR_PROBE_COPY   asr_stream_copy(dst, src, bytes).
+ * Buffers device, 16-byte aligned; bytes a multiple of 16.
+ * Errors: ASR_EINVAL (kind, bytes < 0, NULL), ASR_EALIGN, ASR_EHIP.
+ */
+enum { ASR_PROBE_READ = 0, ASR_PROBE_WRITE = 1, ASR_PROBE_COPY = 2 };
+int asr_hbm_probe(int32_t kind, void* dst, const void* src, int64_t bytes,
+                  void* stream);
+
+/*
+ * Measurement support: the memory traffic of asr_adamw_step over this list
+ * without its arithmetic -- the same launch plan, slots, runs, vector and
+ * element accesses, windows and residency cap, reading param, grad,
+ * exp_avg and exp_avg_sq and writing param, exp_avg and exp_avg_sq of
+ * every element, with param := param XOR grad (for a bf16 param, the high
+ * halves of the upcast values) and the moments written back as read. It
+ * DESTROYS the parameters; it is a bandwidth probe of the step's access
+ * pattern (four streams read, three written), not an optimizer.
+ * Arguments, workspace and errors as for asr_adamw_step.
+ */
+int asr_adamw_stream_probe(const asr_tensor* tensors, int32_t n_tensors,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * Test support: the Box-Muller pair of asr_random_normal from given words:
  * zc[i], zs[i] = r cos(2 pi u2), r sin(2 pi u2) with u1, u2 from
  * w_even[i], w_odd[i] as above -- the same device function, so its error
@@ -313,7 +352,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 105
+#define ASR_ABI_VERSION 106
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,7 @@ Sources (the pages are cited by title and section):
   * "Add stochastic rounding and philox RNG helpers" (FlyDSL pull request),
     Primitives and Tests sections: the add-and-truncate rounding rule and the
     counter-based Philox generator.
-  * The same FlyDSL page, GEMM and Tests sections: a bf16 GEMM whose f32
+  * The same FlyDSL page, Consumer and Tests sections: a bf16 GEMM whose f32
     accumulator is rounded to bf16 by RN or by SR keyed per output element
     (oracle/gemm.py).
   * The same FlyDSL page, discussion section: the generator as a general

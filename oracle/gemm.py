@@ -1,7 +1,7 @@
 """bf16 GEMM with a bf16 output rounded by SR or RN (oracle side).
 
 Source: "Add stochastic rounding and philox RNG helpers" (FlyDSL pull
-request), GEMM section: a bf16 GEMM accumulates in f32 and converts the f32
+request), Consumer section: a bf16 GEMM accumulates in f32 and converts the f32
 accumulator to bf16, by round-to-nearest (the default) or by stochastic
 rounding keyed per output element from a seed; Tests section: the SR output
 stays within tolerance of RN, changes with the seed and is reproducible for
@@ -85,7 +85,7 @@ def f32_sum_bound(a_bits, b_bits):
 def gemm_round(c_f32, rounding, seed=0, step=0, base_index=0):
     """bf16 patterns of an M x N f32 result: "rn" or "sr" (position
     base_index + m*N + n, key (seed, step)). "Add stochastic rounding and
-    philox RNG helpers", GEMM section: the f32 accumulator goes to bf16 by SR
+    philox RNG helpers", Consumer section: the f32 accumulator goes to bf16 by SR
     keyed per output element, RN by default; reading: the position is the
     row-major index."""
     c = np.asarray(c_f32, dtype=np.float32)

@@ -71,3 +71,34 @@ def test_check_disjoint():
         check_disjoint([(8, 8, "inner"), (0, 32, "outer")])  # nested
     with pytest.raises(ValueError):
         check_disjoint([(0, 8, "p"), (0, 8, "p again")])     # identical
+
+
+def test_step_count_passes_2pow24(monkeypatch):
+    """The step count is an integer: past 2**24 (where a float32 count stops
+    moving) each step still passes its own t, so the key (seed, t) changes
+    from step to step ("adamw-sr" page, Method: keyed by (seed, step))."""
+    from adamw_optimizer_stochastic_amd import optim as optim_mod
+    seen = []
+    monkeypatch.setattr(optim_mod.ops, "adamw_step",
+                        lambda *a, **kw: seen.append(kw["step"]))
+    p = torch.nn.Parameter(torch.zeros(6, dtype=torch.bfloat16))
+    p.grad = torch.ones(6, dtype=torch.bfloat16)
+    opt = AdamWSR([p])
+    monkeypatch.setattr(opt, "_workspace", lambda device, numels: None)
+    opt.state[p] = {"step": torch.tensor((1 << 24) - 1, dtype=torch.int64),
+                    "exp_avg": torch.zeros(6), "exp_avg_sq": torch.zeros(6)}
+    opt.step()
+    opt.step()
+    opt.step()
+    assert seen == [1 << 24, (1 << 24) + 1, (1 << 24) + 2]
+    # a state dict keeps the count exactly, above 2**24
+    p2 = torch.nn.Parameter(torch.zeros(6, dtype=torch.bfloat16))
+    opt2 = AdamWSR([p2])
+    opt2.load_state_dict(opt.state_dict())
+    assert int(opt2.state[p2]["step"]) == (1 << 24) + 2
+    assert opt2.state[p2]["step"].dtype == torch.int64
+    # and a count saved by torch's AdamW (a float32 tensor) loads as an int
+    sd = opt.state_dict()
+    sd["state"][0]["step"] = torch.tensor(5.0)
+    opt2.load_state_dict(sd)
+    assert int(opt2.state[p2]["step"]) == 5
