@@ -48,24 +48,44 @@ def hipcc():
 
 
 def build(out_path=LIB_PATH, extra_flags=(), verbose=False):
-    """Compile the library. Always compiles (no up-to-date check)."""
-    fd, tmp = tempfile.mkstemp(prefix=".libadamw_sr.", suffix=".so.tmp",
-                               dir=os.path.dirname(out_path))
+    """Compile the library. Always compiles (no up-to-date check): each
+    source to an object in parallel, then one link."""
+    out_dir = os.path.dirname(out_path)
+    fd, tmp = tempfile.mkstemp(prefix=".libadamw_sr.", suffix=".so.tmp", dir=out_dir)
     os.close(fd)
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
-           *SOURCES, "-o", tmp]
+    objdir = tempfile.mkdtemp(prefix=".libadamw_sr_obj.", dir=out_dir)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    noise = "packed-fp32-ops"  # the host pass does not know the feature
     try:
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        noise = "packed-fp32-ops"  # the host pass does not know the feature
-        msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+        jobs = []
+        for src in SOURCES:
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *compile_flags, *extra_flags, "-I", os.path.join(ROOT, "include"),
+                   "-c", src, "-o", obj]
+            jobs.append((cmd, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                    stderr=subprocess.STDOUT, text=True)))
+        msgs = []
+        failed = []
+        for cmd, obj, proc in jobs:
+            out = proc.communicate()[0]
+            msgs += [ln for ln in out.splitlines() if noise not in ln]
+            if proc.returncode != 0:
+                failed.append(" ".join(cmd))
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed) + "\n" + "\n".join(msgs))
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra_flags,
+                *(obj for _, obj, _ in jobs), "-o", tmp]
+        res = subprocess.run(link, capture_output=True, text=True)
+        msgs += [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
         if res.returncode != 0:
-            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+            raise RuntimeError("link failed:\n" + " ".join(link) + "\n" + "\n".join(msgs))
         if verbose and msgs:
             print("\n".join(msgs))
         os.replace(tmp, out_path)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+        shutil.rmtree(objdir, ignore_errors=True)
     return out_path
 
 

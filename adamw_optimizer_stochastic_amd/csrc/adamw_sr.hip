@@ -85,45 +85,56 @@ struct DevTensor {
   float* v;
   int64_t numel;
   uint64_t base_index;
-  uint32_t vec_ok;      // all four buffers 16-byte aligned: 128-bit path
+  // The tensor is walked in runs of kVec elements; run r covers elements
+  // kVec*r - shift .. kVec*r - shift + kVec - 1, so the first run may start
+  // before element 0 (its leading lanes then touch nothing). shift is chosen
+  // so that every run starts on a vector-aligned address of all four
+  // buffers (16 bytes for f32, 2*kVec bytes for bf16); vec_ok says such a
+  // shift exists, else (buffers misaligned against each other) every
+  // element moves on its own and shift is 0.
+  uint8_t vec_ok;
+  uint8_t shift;
+  uint16_t reserved;
   uint32_t first_slot;  // index of the tensor's first slot within its group
 };
 static_assert(sizeof(DevTensor) == 56, "metadata layout");
 
 enum : int { kRoundSR = ASR_ROUND_SR, kRoundRN = ASR_ROUND_RN };
 
-// One lane's kVec consecutive elements i0 .. i0+kVec-1 of tensor t (count of
-// them inside the tensor: 0..kVec). VEC: the tensor's buffers are 16-byte
-// aligned, so a full run moves with vector accesses (128-bit for f32; 128- or
-// 64-bit for bf16); otherwise element by element.
+// One lane's run of kVec consecutive elements i0 .. i0+kVec-1 of tensor t,
+// of which lo <= e < hi lie inside the tensor (i0 < 0 only for the first run
+// of a shifted tensor). VEC: the run starts on a vector-aligned address of
+// all four buffers, so a whole run moves with vector accesses (128-bit for
+// f32; 64- or 128-bit for bf16); a cut run, or a tensor without such a
+// shift, moves element by element.
 template <class PT, class GT, int ROUND, int PHASE, bool VEC>
-__device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int count,
+__device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int lo, int hi,
                                            const Coeffs& c, uint32_t seed, uint32_t step) {
   using PS = typename PT::storage;
   using GS = typename GT::storage;
-  PS* __restrict__ param = static_cast<PS*>(t.param) + i0;
-  const GS* __restrict__ grad = static_cast<const GS*>(t.grad) + i0;
-  float* __restrict__ m = t.m + i0;
-  float* __restrict__ v = t.v + i0;
-  const bool full = VEC && count == kVec;
+  PS* __restrict__ param = static_cast<PS*>(t.param);
+  const GS* __restrict__ grad = static_cast<const GS*>(t.grad);
+  float* __restrict__ m = t.m;
+  float* __restrict__ v = t.v;
+  const bool full = VEC && lo == 0 && hi == kVec;
   float p[kVec], g[kVec], mm[kVec], vv[kVec];
   if (full) {
-    load_vec<kNonTemporal, kVec>(param, p);
-    load_vec<kNonTemporal, kVec>(grad, g);
-    load_vec<kNonTemporal, kVec>(m, mm);
-    load_vec<kNonTemporal, kVec>(v, vv);
+    load_vec<kNonTemporal, kVec>(param + i0, p);
+    load_vec<kNonTemporal, kVec>(grad + i0, g);
+    load_vec<kNonTemporal, kVec>(m + i0, mm);
+    load_vec<kNonTemporal, kVec>(v + i0, vv);
   } else {
-    load_n(param, count, p);
-    load_n(grad, count, g);
-    load_n(m, count, mm);
-    load_n(v, count, vv);
+    load_range(param, i0, lo, hi, p);
+    load_range(grad, i0, lo, hi, g);
+    load_range(m, i0, lo, hi, mm);
+    load_range(v, i0, lo, hi, vv);
   }
 #pragma unroll
   for (int e = 0; e < kVec; ++e) adamw_update(p[e], g[e], mm[e], vv[e], c);
 
   if constexpr (std::is_same_v<PT, F32>) {
-    if (full) store_vec<kNonTemporal, kVec>(param, p);
-    else store_n(param, count, p);
+    if (full) store_vec<kNonTemporal, kVec>(param + i0, p);
+    else store_range(param, i0, lo, hi, p);
   } else {
     uint32_t h[kVec];
     if constexpr (ROUND == kRoundSR) {
@@ -135,44 +146,48 @@ __device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int co
 #pragma unroll
       for (int e = 0; e < kVec; ++e) h[e] = round_rn(__float_as_uint(p[e]));
     }
-    if (full) store_vec_bf16<kNonTemporal, kVec>(param, h);
-    else store_n_bf16(param, count, h);
+    if (full) store_vec_bf16<kNonTemporal, kVec>(param + i0, h);
+    else store_range_bf16(param, i0, lo, hi, h);
   }
   if (full) {
-    store_vec<kNonTemporal, kVec>(m, mm);
-    store_vec<kNonTemporal, kVec>(v, vv);
+    store_vec<kNonTemporal, kVec>(m + i0, mm);
+    store_vec<kNonTemporal, kVec>(v + i0, vv);
   } else {
-    store_n(m, count, mm);
-    store_n(v, count, vv);
+    store_range(m, i0, lo, hi, mm);
+    store_range(v, i0, lo, hi, vv);
   }
 }
 
+// The phase of a run's first position within its Philox call, (base_index
+// + i0) & 3, is the same for every run of a tensor: (base_index - shift) & 3.
 template <class PT, class GT, int ROUND, bool VEC>
-__device__ __forceinline__ void adamw_run_phase(const DevTensor& t, int64_t i0, int count,
+__device__ __forceinline__ void adamw_run_phase(const DevTensor& t, int64_t i0, int lo, int hi,
                                                  const Coeffs& c, uint32_t seed, uint32_t step) {
   if constexpr (std::is_same_v<PT, BF16> && ROUND == kRoundSR) {
-    switch (static_cast<int>(t.base_index & 3u)) {
-      case 0: adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, count, c, seed, step); break;
-      case 1: adamw_run<PT, GT, ROUND, 1, VEC>(t, i0, count, c, seed, step); break;
-      case 2: adamw_run<PT, GT, ROUND, 2, VEC>(t, i0, count, c, seed, step); break;
-      default: adamw_run<PT, GT, ROUND, 3, VEC>(t, i0, count, c, seed, step); break;
+    switch (static_cast<int>((t.base_index - t.shift) & 3u)) {
+      case 0: adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, lo, hi, c, seed, step); break;
+      case 1: adamw_run<PT, GT, ROUND, 1, VEC>(t, i0, lo, hi, c, seed, step); break;
+      case 2: adamw_run<PT, GT, ROUND, 2, VEC>(t, i0, lo, hi, c, seed, step); break;
+      default: adamw_run<PT, GT, ROUND, 3, VEC>(t, i0, lo, hi, c, seed, step); break;
     }
   } else {
-    adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, count, c, seed, step);
+    adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, lo, hi, c, seed, step);
   }
 }
 
 // Slot `local` (kSlot elements) of tensor t: one kVec-element run per lane.
-// Lanes past the end of a short last slot get count 0 and touch nothing (no
-// early exit, so the whole descriptor is fetched in one round).
+// Lanes past the end of a short last slot get an empty range and touch
+// nothing (no early exit, so the whole descriptor is fetched in one round).
 template <class PT, class GT, int ROUND>
 __device__ __forceinline__ void adamw_slot(const DevTensor& t, uint32_t local, const Coeffs& c,
                                            uint32_t seed, uint32_t step) {
-  const int64_t i0 = static_cast<int64_t>(local) * kSlot + static_cast<int64_t>(threadIdx.x) * kVec;
+  const int64_t i0 = static_cast<int64_t>(local) * kSlot +
+                     static_cast<int64_t>(threadIdx.x) * kVec - static_cast<int64_t>(t.shift);
   const int64_t left = t.numel - i0;
-  const int count = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
-  if (t.vec_ok) adamw_run_phase<PT, GT, ROUND, true>(t, i0, count, c, seed, step);
-  else adamw_run_phase<PT, GT, ROUND, false>(t, i0, count, c, seed, step);
+  const int hi = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
+  const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
+  if (t.vec_ok) adamw_run_phase<PT, GT, ROUND, true>(t, i0, lo, hi, c, seed, step);
+  else adamw_run_phase<PT, GT, ROUND, false>(t, i0, lo, hi, c, seed, step);
 }
 
 // The multi-tensor step, one slot per workgroup, no loop: the workgroups in
@@ -280,16 +295,18 @@ philox_fill(uint32_t* __restrict__ out, int64_t n_counters, uint64_t counter_bas
 }
 
 // ------------------------------------------------------ f32 -> bf16 converts
-// One lane's kCvtVec elements i0 .. of the conversion (count inside: 0..V).
+// One lane's run of kCvtVec elements i0 .. of the conversion, of which
+// lo <= e < hi lie inside the array (i0 < 0 only for the first run when the
+// runs are shifted, as for the step).
 template <int ROUND, int PHASE, bool VEC>
 __device__ __forceinline__ void convert_run(const float* __restrict__ in,
-                                            uint16_t* __restrict__ out, int64_t i0, int count,
+                                            uint16_t* __restrict__ out, int64_t i0, int lo, int hi,
                                             uint64_t base_index, uint32_t seed, uint32_t step) {
   constexpr int V = kCvtVec;
-  const bool full = VEC && count == V;
+  const bool full = VEC && lo == 0 && hi == V;
   float x[V];
   if (full) load_vec<kNonTemporal, V>(in + i0, x);
-  else load_n(in + i0, count, x);
+  else load_range(in, i0, lo, hi, x);
   uint32_t h[V];
   if constexpr (ROUND == kRoundSR) {
     uint32_t r[V];
@@ -301,7 +318,7 @@ __device__ __forceinline__ void convert_run(const float* __restrict__ in,
     for (int e = 0; e < V; ++e) h[e] = round_rn(__float_as_uint(x[e]));
   }
   if (full) store_vec_bf16<kNonTemporal, V>(out + i0, h);
-  else store_n_bf16(out + i0, count, h);
+  else store_range_bf16(out, i0, lo, hi, h);
 }
 
 #ifndef ASR_CVT_WINDOWS
@@ -323,34 +340,40 @@ __device__ __forceinline__ uint32_t cvt_slot_of_block(uint32_t b, uint32_t grid)
 }
 
 // One slot of kCvtSlot elements per workgroup, no loop (as for the step).
+// shift: elements the runs start before in[0] (the first run's leading
+// lanes touch nothing), chosen so that whole runs are vector-aligned in both
+// buffers; vec_ok says such a shift exists (else shift is 0 and every
+// element moves on its own).
 template <int ROUND>
 __global__ void __launch_bounds__(kBlock)
 convert_f32_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n,
-                 uint64_t slot0, uint64_t base_index, uint32_t seed, uint32_t step, int vec_ok) {
+                 uint64_t slot0, uint64_t base_index, uint32_t seed, uint32_t step, int vec_ok,
+                 int shift) {
   const int64_t i0 = static_cast<int64_t>(slot0 + cvt_slot_of_block(blockIdx.x, gridDim.x)) * kCvtSlot +
-                     static_cast<int64_t>(threadIdx.x) * kCvtVec;
+                     static_cast<int64_t>(threadIdx.x) * kCvtVec - shift;
   const int64_t left = n - i0;
-  const int count = left <= 0 ? 0 : (left < kCvtVec ? static_cast<int>(left) : kCvtVec);
+  const int hi = left <= 0 ? 0 : (left < kCvtVec ? static_cast<int>(left) : kCvtVec);
+  const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
   if constexpr (ROUND == kRoundSR) {
-    const int phase = static_cast<int>(base_index & 3u);
+    const int phase = static_cast<int>((base_index - static_cast<uint64_t>(shift)) & 3u);
     if (vec_ok) {
       switch (phase) {
-        case 0: convert_run<ROUND, 0, true>(in, out, i0, count, base_index, seed, step); break;
-        case 1: convert_run<ROUND, 1, true>(in, out, i0, count, base_index, seed, step); break;
-        case 2: convert_run<ROUND, 2, true>(in, out, i0, count, base_index, seed, step); break;
-        default: convert_run<ROUND, 3, true>(in, out, i0, count, base_index, seed, step); break;
+        case 0: convert_run<ROUND, 0, true>(in, out, i0, lo, hi, base_index, seed, step); break;
+        case 1: convert_run<ROUND, 1, true>(in, out, i0, lo, hi, base_index, seed, step); break;
+        case 2: convert_run<ROUND, 2, true>(in, out, i0, lo, hi, base_index, seed, step); break;
+        default: convert_run<ROUND, 3, true>(in, out, i0, lo, hi, base_index, seed, step); break;
       }
     } else {
       switch (phase) {
-        case 0: convert_run<ROUND, 0, false>(in, out, i0, count, base_index, seed, step); break;
-        case 1: convert_run<ROUND, 1, false>(in, out, i0, count, base_index, seed, step); break;
-        case 2: convert_run<ROUND, 2, false>(in, out, i0, count, base_index, seed, step); break;
-        default: convert_run<ROUND, 3, false>(in, out, i0, count, base_index, seed, step); break;
+        case 0: convert_run<ROUND, 0, false>(in, out, i0, lo, hi, base_index, seed, step); break;
+        case 1: convert_run<ROUND, 1, false>(in, out, i0, lo, hi, base_index, seed, step); break;
+        case 2: convert_run<ROUND, 2, false>(in, out, i0, lo, hi, base_index, seed, step); break;
+        default: convert_run<ROUND, 3, false>(in, out, i0, lo, hi, base_index, seed, step); break;
       }
     }
   } else {
-    if (vec_ok) convert_run<ROUND, 0, true>(in, out, i0, count, base_index, seed, step);
-    else convert_run<ROUND, 0, false>(in, out, i0, count, base_index, seed, step);
+    if (vec_ok) convert_run<ROUND, 0, true>(in, out, i0, lo, hi, base_index, seed, step);
+    else convert_run<ROUND, 0, false>(in, out, i0, lo, hi, base_index, seed, step);
   }
 }
 
@@ -373,6 +396,117 @@ stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16
 #pragma unroll
   for (int k = 0; k < kCopyVec; ++k)
     if (base + k * kBlock < n16) dst[base + k * kBlock] = x[k];
+}
+
+// A read-only and a write-only stream in the copy's form (one 16 KiB slot
+// per workgroup, windows, residency cap). The read keeps its loads alive by
+// XOR-ing them and storing the result to sink[0] only if it equals a value
+// that a buffer of equal 16-byte words (the benchmark fills it so) cannot
+// give, so it moves no bytes to memory.
+__global__ void __launch_bounds__(kBlock)
+stream_read(const u32x4* __restrict__ src, u32x4* __restrict__ sink, uint64_t n16,
+            uint64_t slot0) {
+  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kBlock * kCopyVec) +
+                        threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < kCopyVec; ++k)
+    if (base + k * kBlock < n16) acc ^= src[base + k * kBlock];
+  if (acc.x == 0x9E3779B9u && acc.y == 0xBB67AE85u && acc.z == 0xD2511F53u &&
+      acc.w == 0xCD9E8D57u)
+    sink[0] = acc;
+}
+
+__global__ void __launch_bounds__(kBlock)
+stream_write(u32x4* __restrict__ dst, uint64_t n16, uint64_t slot0, uint32_t value) {
+  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kBlock * kCopyVec) +
+                        threadIdx.x;
+  const u32x4 x = {value, value, value, value};
+#pragma unroll
+  for (int k = 0; k < kCopyVec; ++k)
+    if (base + k * kBlock < n16) dst[base + k * kBlock] = x;
+}
+
+// The step's memory traffic with its arithmetic taken out: the same runs,
+// vector and element accesses, slots, windows and residency cap as
+// adamw_run, but the new parameter is the old one XOR the gradient (the
+// high halves, for a bf16 parameter) and m and v are written back as read.
+// It measures what HBM gives this access pattern (four streams read, three
+// written) under the step's launch structure; the benchmark reports it
+// beside the step.
+template <class PT, class GT, bool VEC>
+__device__ __forceinline__ void probe_run(const DevTensor& t, int64_t i0, int lo, int hi) {
+  using PS = typename PT::storage;
+  using GS = typename GT::storage;
+  PS* __restrict__ param = static_cast<PS*>(t.param);
+  const GS* __restrict__ grad = static_cast<const GS*>(t.grad);
+  float* __restrict__ m = t.m;
+  float* __restrict__ v = t.v;
+  const bool full = VEC && lo == 0 && hi == kVec;
+  float p[kVec], g[kVec], mm[kVec], vv[kVec];
+  if (full) {
+    load_vec<kNonTemporal, kVec>(param + i0, p);
+    load_vec<kNonTemporal, kVec>(grad + i0, g);
+    load_vec<kNonTemporal, kVec>(m + i0, mm);
+    load_vec<kNonTemporal, kVec>(v + i0, vv);
+  } else {
+    load_range(param, i0, lo, hi, p);
+    load_range(grad, i0, lo, hi, g);
+    load_range(m, i0, lo, hi, mm);
+    load_range(v, i0, lo, hi, vv);
+  }
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) p[e] = __uint_as_float(__float_as_uint(p[e]) ^ __float_as_uint(g[e]));
+  if constexpr (std::is_same_v<PT, F32>) {
+    if (full) store_vec<kNonTemporal, kVec>(param + i0, p);
+    else store_range(param, i0, lo, hi, p);
+  } else {
+    uint32_t h[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) h[e] = __float_as_uint(p[e]) >> 16;
+    if (full) store_vec_bf16<kNonTemporal, kVec>(param + i0, h);
+    else store_range_bf16(param, i0, lo, hi, h);
+  }
+  if (full) {
+    store_vec<kNonTemporal, kVec>(m + i0, mm);
+    store_vec<kNonTemporal, kVec>(v + i0, vv);
+  } else {
+    store_range(m, i0, lo, hi, mm);
+    store_range(v, i0, lo, hi, vv);
+  }
+}
+
+template <class PT, class GT>
+__device__ __forceinline__ void probe_slot(const DevTensor& t, uint32_t local) {
+  const int64_t i0 = static_cast<int64_t>(local) * kSlot +
+                     static_cast<int64_t>(threadIdx.x) * kVec - static_cast<int64_t>(t.shift);
+  const int64_t left = t.numel - i0;
+  const int hi = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
+  const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
+  if (t.vec_ok) probe_run<PT, GT, true>(t, i0, lo, hi);
+  else probe_run<PT, GT, false>(t, i0, lo, hi);
+}
+
+// Launched exactly like adamw_sr_class / adamw_sr_slots (same arguments;
+// the coefficients, seed and step are unused).
+template <class PT, class GT>
+__global__ void __launch_bounds__(kBlock)
+stream_probe_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_tensor,
+                   uint32_t magic, uint32_t slot0, Coeffs, uint32_t, uint32_t) {
+  const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
+  uint32_t ti = __umulhi(slot, magic);
+  if (static_cast<uint64_t>(ti + 1) * slots_per_tensor <= slot) ++ti;
+  const DevTensor t = tensors[ti];
+  probe_slot<PT, GT>(t, slot - ti * slots_per_tensor);
+}
+
+template <class PT, class GT>
+__global__ void __launch_bounds__(kBlock)
+stream_probe_slots(const DevTensor* __restrict__ tensors, const uint32_t* __restrict__ slot_tensor,
+                   uint32_t slot0, Coeffs, uint32_t, uint32_t) {
+  const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
+  const DevTensor t = tensors[slot_tensor[slot]];
+  probe_slot<PT, GT>(t, slot - t.first_slot);
 }
 
 // ---------------------------------------------- SR with caller's bits
@@ -500,8 +634,37 @@ uint64_t slots_of(int64_t numel) {
   return (static_cast<uint64_t>(numel) + asr::kSlot - 1) / asr::kSlot;
 }
 
+// Slots of a tensor: its runs start `shift` elements before element 0.
+uint64_t tensor_slots(const asr::DevTensor& d) { return slots_of(d.numel + d.shift); }
+
+// The most slots a tensor of this size can take, whatever its shift (the
+// workspace size must not depend on where the buffers are).
+uint64_t max_slots(int64_t numel) { return slots_of(numel + asr::kVec - 1); }
+
+// Whether element s of a buffer of this dtype (and so every kVec-th element
+// from there) starts a vector access: 16 bytes for f32 (one or two 128-bit
+// accesses), 2*kVec bytes for bf16.
+bool run_aligned(const void* p, int32_t dtype, int s) {
+  const uintptr_t elem = dtype == ASR_F32 ? 4 : 2;
+  const uintptr_t vec = dtype == ASR_F32 ? 16 : 2 * asr::kVec;
+  return ((reinterpret_cast<uintptr_t>(p) + (asr::kVec - s) * elem) & (vec - 1)) == 0;
+}
+
+// The shift 0 <= s < kVec for which runs starting at elements k*kVec - s
+// are vector-aligned in all four buffers of the tensor, or -1 (buffers
+// misaligned against each other: the tensor goes element by element). A
+// piece cut from aligned buffers at any element offset o has one: s =
+// o mod kVec.
+int vector_shift(const asr_tensor& t) {
+  for (int s = 0; s < asr::kVec; ++s)
+    if (run_aligned(t.param, t.param_dtype, s) && run_aligned(t.grad, t.grad_dtype, s) &&
+        run_aligned(t.exp_avg, ASR_F32, s) && run_aligned(t.exp_avg_sq, ASR_F32, s))
+      return s;
+  return -1;
+}
+
 // A (param dtype, grad dtype) pair's tensors are launched as size classes
-// (equal numel, at least kClassMinSlots slots in total; up to
+// (equal slot counts, at least kClassMinSlots slots in total; up to
 // kMaxClassLaunches per pair) plus one table-driven launch for the rest.
 constexpr uint64_t kClassMinSlots = 2048;
 constexpr int kMaxClassLaunches = 64;
@@ -535,13 +698,13 @@ std::string plan_launches(const std::vector<asr::DevTensor> (&group)[asr::kGroup
                           std::vector<Launch>* out) {
   for (int g = 0; g < asr::kGroups; ++g) {
     if (group[g].empty()) continue;
-    std::map<int64_t, std::vector<size_t>> by_numel;
-    for (size_t i = 0; i < group[g].size(); ++i) by_numel[group[g][i].numel].push_back(i);
+    std::map<uint64_t, std::vector<size_t>> by_slots;
+    for (size_t i = 0; i < group[g].size(); ++i)
+      by_slots[tensor_slots(group[g][i])].push_back(i);
     Launch rest;
     rest.group = g;
     int classes = 0;
-    for (const auto& [numel, idx] : by_numel) {
-      const uint64_t per = slots_of(numel);
+    for (const auto& [per, idx] : by_slots) {
       const uint64_t total = per * idx.size();
       if (total >= kClassMinSlots && classes < kMaxClassLaunches) {
         if (total > 0xFFFFFFFFull) return "more than 2**32 slots of one size";
@@ -562,7 +725,7 @@ std::string plan_launches(const std::vector<asr::DevTensor> (&group)[asr::kGroup
           asr::DevTensor d = group[g][i];
           d.first_slot = static_cast<uint32_t>(rest.n_slots);
           rest.tensors.push_back(d);
-          rest.n_slots += per;
+          rest.n_slots += per;  // = tensor_slots(d)
           if (rest.n_slots > 0xFFFFFFFFull) return "more than 2**32 slots of mixed sizes";
         }
       }
@@ -599,6 +762,15 @@ template <class PT, class GT, int R>
 struct PickClass {
   static ClassKernel get() { return asr::adamw_sr_class<PT, GT, R>; }
 };
+// the traffic probe of the same launch (the rounding does not apply)
+template <class PT, class GT, int>
+struct PickProbeTable {
+  static TableKernel get() { return asr::stream_probe_slots<PT, GT>; }
+};
+template <class PT, class GT, int>
+struct PickProbeClass {
+  static ClassKernel get() { return asr::stream_probe_class<PT, GT>; }
+};
 
 // LDS reserved per workgroup to hold the step kernel at kBlocksPerCU
 // resident workgroups per CU (0 = no cap).
@@ -612,16 +784,17 @@ hipError_t occupancy_lds(const void* kernel, uint32_t* lds) {
   return hipSuccess;
 }
 
-// One launch of the plan: (table launches) the slot table, then the step in
-// launches of at most kMaxGrid slots.
-hipError_t run_launch(const Launch& l, uint8_t* ws, int rounding, const asr::Coeffs& c,
-                      uint32_t seed, uint32_t step, hipStream_t stream) {
+// One launch of the plan: (table launches) the slot table, then the step (or
+// the traffic probe) in launches of at most kMaxGrid slots.
+hipError_t run_launch(const Launch& l, uint8_t* ws, bool probe, int rounding,
+                      const asr::Coeffs& c, uint32_t seed, uint32_t step, hipStream_t stream) {
   const auto* d_tensors = reinterpret_cast<const asr::DevTensor*>(ws + l.tensors_off);
   const uint32_t n_slots = static_cast<uint32_t>(l.n_slots);
   hipError_t e;
   uint32_t lds = 0;
   if (l.by_class) {
-    const ClassKernel k = pick_kernel<PickClass>(l.group, rounding);
+    const ClassKernel k = probe ? pick_kernel<PickProbeClass>(l.group, rounding)
+                                : pick_kernel<PickClass>(l.group, rounding);
     if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
     const uint32_t magic = 0xFFFFFFFFu / l.slots_per_tensor;
     for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
@@ -638,7 +811,8 @@ hipError_t run_launch(const Launch& l, uint8_t* ws, int rounding, const asr::Coe
              reinterpret_cast<const uint32_t*>(ws + l.first_off),
              static_cast<int32_t>(l.tensors.size()), d_table, n_slots);
   if (e != hipSuccess) return e;
-  const TableKernel k = pick_kernel<PickTable>(l.group, rounding);
+  const TableKernel k = probe ? pick_kernel<PickProbeTable>(l.group, rounding)
+                              : pick_kernel<PickTable>(l.group, rounding);
   if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
   for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
     const uint32_t grid = std::min(n_slots - slot0, asr::kMaxGrid);
@@ -649,45 +823,26 @@ hipError_t run_launch(const Launch& l, uint8_t* ws, int rounding, const asr::Coe
   return hipSuccess;
 }
 
-}  // namespace
+// ------------------------------------------------------------- the plan
+// What one step call enqueues: the launches and the metadata image that is
+// uploaded to the front of the workspace (device-filled slot tables follow).
+struct StepPlan {
+  std::vector<Launch> launches;
+  std::vector<uint8_t> image;  // metadata, uploaded to workspace[0, meta_bytes)
+  size_t used_bytes = 0;       // workspace bytes this plan writes (metadata + tables)
+  size_t bound_bytes = 0;      // asr_adamw_workspace_bytes of the list
+};
 
-extern "C" {
-
-int asr_abi_version(void) { return ASR_ABI_VERSION; }
-
-const char* asr_last_error(void) { return asr_host::g_last_error.c_str(); }
-
-size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors) {
-  if (n_tensors <= 0 || !tensors) return 0;
-  uint64_t slots = 0;
-  for (int32_t i = 0; i < n_tensors; ++i)
-    if (tensors[i].numel > 0) slots += slots_of(tensors[i].numel);
-  return workspace_bound(n_tensors, slots);
-}
-
-int asr_adamw_host_scalars(double lr, double beta1, double beta2, double eps,
-                           double weight_decay, int64_t step, float* out) {
-  if (int s = check_hparams(lr, beta1, beta2, eps, weight_decay, step)) return s;
-  if (!out) return fail(ASR_EINVAL, "out is NULL");
-  const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
-  const float vals[8] = {c.decay, c.b1, c.omb1, c.b2, c.omb2, c.step_size, c.inv_bc2_sqrt, c.eps};
-  std::memcpy(out, vals, sizeof(vals));
-  return ok();
-}
-
-int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, double beta1,
-                   double beta2, double eps, double weight_decay, int64_t step,
-                   uint32_t seed, int32_t rounding, void* workspace,
-                   size_t workspace_bytes, void* stream_ptr) {
+// Validates the list (statuses and messages as documented for
+// asr_adamw_step), groups it by dtype pair, plans the launches and lays out
+// the workspace. An all-empty list gives a plan without launches.
+int make_plan(const asr_tensor* tensors, int32_t n_tensors, StepPlan* plan) {
   if (n_tensors < 0) return fail(ASR_EINVAL, "n_tensors < 0");
   if (n_tensors > 0 && !tensors) return fail(ASR_EINVAL, "tensors is NULL");
-  if (int s = check_hparams(lr, beta1, beta2, eps, weight_decay, step)) return s;
-  if (rounding != ASR_ROUND_SR && rounding != ASR_ROUND_RN)
-    return fail(ASR_EINVAL, "rounding must be ASR_ROUND_SR or ASR_ROUND_RN");
-
   // Validate and sort into dtype groups; drop empty tensors.
   std::vector<asr::DevTensor> group[asr::kGroups];
   uint64_t group_slots[asr::kGroups] = {0, 0, 0, 0};
+  uint64_t bound_slots = 0;
   for (int32_t i = 0; i < n_tensors; ++i) {
     const asr_tensor& t = tensors[i];
     const std::string at = "tensor " + std::to_string(i) + ": ";
@@ -711,31 +866,24 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, doub
     d.v = t.exp_avg_sq;
     d.numel = t.numel;
     d.base_index = t.base_index;
-    d.vec_ok = aligned(t.param, 16) && aligned(t.grad, 16) && aligned(t.exp_avg, 16) &&
-               aligned(t.exp_avg_sq, 16);
+    const int shift = vector_shift(t);
+    d.vec_ok = shift >= 0;
+    d.shift = static_cast<uint8_t>(shift >= 0 ? shift : 0);
+    d.reserved = 0;
     d.first_slot = 0;  // set by the launch plan
     group[g].push_back(d);
-    group_slots[g] += slots_of(t.numel);
+    group_slots[g] += tensor_slots(d);
+    bound_slots += max_slots(t.numel);
     if (group_slots[g] > 0xFFFFFFFFull)
       return fail(ASR_EINVAL, "more than 2**32 slots of one dtype pair");
   }
-  uint64_t total_slots = 0;
-  for (int g = 0; g < asr::kGroups; ++g) total_slots += group_slots[g];
-  if (total_slots == 0) return ok();
-
-  const size_t need = workspace_bound(n_tensors, total_slots);
-  if (!workspace || workspace_bytes < need)
-    return fail(ASR_EWORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
-  if (!aligned(workspace, 16)) return fail(ASR_EWORKSPACE, "workspace not 16-byte aligned");
-
-  std::vector<Launch> launches;
-  const std::string err = plan_launches(group, &launches);
+  plan->bound_bytes = workspace_bound(n_tensors, bound_slots);
+  const std::string err = plan_launches(group, &plan->launches);
   if (!err.empty()) return fail(ASR_EINVAL, err);
-  const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
 
   // Workspace offsets: uploaded metadata first, device-filled tables after.
   size_t off = 0;
-  for (Launch& l : launches) {
+  for (Launch& l : plan->launches) {
     off = align_up(off, 16);
     l.tensors_off = off;
     off += l.tensors.size() * sizeof(asr::DevTensor);
@@ -747,40 +895,106 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, doub
   }
   const size_t meta_bytes = align_up(off, 16);
   off = meta_bytes;
-  for (Launch& l : launches) {
+  for (Launch& l : plan->launches) {
     if (l.by_class) continue;
     off = align_up(off, 16);
     l.table_off = off;
     off += l.n_slots * sizeof(uint32_t);
   }
-  if (off > need) return fail(ASR_EWORKSPACE, "internal: workspace plan exceeds its bound");
-  std::vector<uint8_t> image(meta_bytes, 0);
-  for (const Launch& l : launches) {
-    std::memcpy(image.data() + l.tensors_off, l.tensors.data(),
+  plan->used_bytes = off;
+  if (!plan->launches.empty() && off > plan->bound_bytes)
+    return fail(ASR_EWORKSPACE, "internal: workspace plan exceeds its bound");
+  plan->image.assign(meta_bytes, 0);
+  for (const Launch& l : plan->launches) {
+    std::memcpy(plan->image.data() + l.tensors_off, l.tensors.data(),
                 l.tensors.size() * sizeof(asr::DevTensor));
     if (!l.by_class)
       for (size_t k = 0; k < l.tensors.size(); ++k)
-        std::memcpy(image.data() + l.first_off + k * sizeof(uint32_t), &l.tensors[k].first_slot,
-                    sizeof(uint32_t));
+        std::memcpy(plan->image.data() + l.first_off + k * sizeof(uint32_t),
+                    &l.tensors[k].first_slot, sizeof(uint32_t));
   }
+  return ASR_OK;
+}
 
-  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+int check_workspace(const StepPlan& plan, const void* workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < plan.bound_bytes)
+    return fail(ASR_EWORKSPACE, "workspace needs " + std::to_string(plan.bound_bytes) + " bytes");
+  if (!aligned(workspace, 16)) return fail(ASR_EWORKSPACE, "workspace not 16-byte aligned");
+  return ASR_OK;
+}
+
+// Uploads the metadata to ws (kernel-argument copies: stream-ordered,
+// allocation-free) and enqueues every launch of the plan on the stream.
+int enqueue_plan(const StepPlan& plan, uint8_t* ws, bool probe, int rounding,
+                 const asr::Coeffs& c, uint32_t seed, uint32_t step, hipStream_t stream) {
+  const size_t meta_bytes = plan.image.size();
   for (size_t pos = 0; pos < meta_bytes; pos += asr::kUploadWords * sizeof(uint32_t)) {
     asr::UploadBlock blk;
     const size_t bytes = std::min(meta_bytes - pos, sizeof(blk.w));
     std::memset(blk.w, 0, sizeof(blk.w));
-    std::memcpy(blk.w, image.data() + pos, bytes);
+    std::memcpy(blk.w, plan.image.data() + pos, bytes);
     hipError_t e = launch(asr::upload_words, 1, stream, blk,
                           reinterpret_cast<uint32_t*>(ws + pos),
                           static_cast<uint32_t>(bytes / sizeof(uint32_t)));
     if (e != hipSuccess) return hip_fail(e, "metadata upload launch");
   }
-  for (const Launch& l : launches) {
-    hipError_t e = run_launch(l, ws, rounding, c, seed, static_cast<uint32_t>(step), stream);
-    if (e != hipSuccess) return hip_fail(e, "adamw kernel launch");
+  for (const Launch& l : plan.launches) {
+    hipError_t e = run_launch(l, ws, probe, rounding, c, seed, step, stream);
+    if (e != hipSuccess) return hip_fail(e, probe ? "probe kernel launch" : "adamw kernel launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int asr_abi_version(void) { return ASR_ABI_VERSION; }
+
+const char* asr_last_error(void) { return asr_host::g_last_error.c_str(); }
+
+size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors) {
+  if (n_tensors <= 0 || !tensors) return 0;
+  uint64_t slots = 0;
+  for (int32_t i = 0; i < n_tensors; ++i)
+    if (tensors[i].numel > 0) slots += max_slots(tensors[i].numel);
+  return workspace_bound(n_tensors, slots);
+}
+
+int asr_adamw_host_scalars(double lr, double beta1, double beta2, double eps,
+                           double weight_decay, int64_t step, float* out) {
+  if (int s = check_hparams(lr, beta1, beta2, eps, weight_decay, step)) return s;
+  if (!out) return fail(ASR_EINVAL, "out is NULL");
+  const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
+  const float vals[8] = {c.decay, c.b1, c.omb1, c.b2, c.omb2, c.step_size, c.inv_bc2_sqrt, c.eps};
+  std::memcpy(out, vals, sizeof(vals));
+  return ok();
+}
+
+int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, double beta1,
+                   double beta2, double eps, double weight_decay, int64_t step,
+                   uint32_t seed, int32_t rounding, void* workspace,
+                   size_t workspace_bytes, void* stream_ptr) {
+  if (int s = check_hparams(lr, beta1, beta2, eps, weight_decay, step)) return s;
+  if (rounding != ASR_ROUND_SR && rounding != ASR_ROUND_RN)
+    return fail(ASR_EINVAL, "rounding must be ASR_ROUND_SR or ASR_ROUND_RN");
+  StepPlan plan;
+  if (int s = make_plan(tensors, n_tensors, &plan)) return s;
+  if (plan.launches.empty()) return ok();
+  if (int s = check_workspace(plan, workspace, workspace_bytes)) return s;
+  const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
+  return enqueue_plan(plan, static_cast<uint8_t*>(workspace), false, rounding, c, seed,
+                      static_cast<uint32_t>(step), static_cast<hipStream_t>(stream_ptr));
+}
+
+int asr_adamw_stream_probe(const asr_tensor* tensors, int32_t n_tensors, void* workspace,
+                           size_t workspace_bytes, void* stream_ptr) {
+  StepPlan plan;
+  if (int s = make_plan(tensors, n_tensors, &plan)) return s;
+  if (plan.launches.empty()) return ok();
+  if (int s = check_workspace(plan, workspace, workspace_bytes)) return s;
+  return enqueue_plan(plan, static_cast<uint8_t*>(workspace), true, ASR_ROUND_SR, asr::Coeffs{},
+                      0, 0, static_cast<hipStream_t>(stream_ptr));
 }
 
 int asr_philox_4x32_fill(uint32_t* out, int64_t n_counters, uint64_t counter_base,
@@ -809,10 +1023,21 @@ static int convert(int rounding, const float* in, uint16_t* out, int64_t n, uint
   if (!aligned(in, 4) || !aligned(out, 2))
     return fail(ASR_EALIGN, "buffer not aligned to its element size");
   if (n > (int64_t{1} << 62)) return fail(ASR_EINVAL, "n too large");
-  const uint64_t n_slots = (static_cast<uint64_t>(n) + asr::kCvtSlot - 1) / asr::kCvtSlot;
-  const int vec_ok = aligned(in, 16) && aligned(out, 16);
+  // runs of kCvtVec elements start `shift` elements before in[0], on
+  // 16-byte addresses of both buffers if some shift allows it
+  int shift = -1;
+  for (int s = 0; s < asr::kCvtVec && shift < 0; ++s) {
+    const uintptr_t ia = reinterpret_cast<uintptr_t>(in) + (asr::kCvtVec - s) * 4;
+    const uintptr_t oa = reinterpret_cast<uintptr_t>(out) + (asr::kCvtVec - s) * 2;
+    if ((ia & 15) == 0 && (oa & (2 * asr::kCvtVec - 1)) == 0) shift = s;
+  }
+  const int vec_ok = shift >= 0;
+  if (shift < 0) shift = 0;
+  const uint64_t n_slots =
+      (static_cast<uint64_t>(n) + static_cast<uint64_t>(shift) + asr::kCvtSlot - 1) / asr::kCvtSlot;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  using K = void (*)(const float*, uint16_t*, int64_t, uint64_t, uint64_t, uint32_t, uint32_t, int);
+  using K = void (*)(const float*, uint16_t*, int64_t, uint64_t, uint64_t, uint32_t, uint32_t, int,
+                     int);
   const K k = rounding == ASR_ROUND_SR ? asr::convert_f32_bf16<asr::kRoundSR>
                                        : asr::convert_f32_bf16<asr::kRoundRN>;
   uint32_t lds = 0;
@@ -828,7 +1053,7 @@ static int convert(int rounding, const float* in, uint16_t* out, int64_t n, uint
   for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
     hipError_t e = launch_lds(k, grid, lds, stream, in, out, n, slot0, base_index, seed, step,
-                              vec_ok);
+                              vec_ok, shift);
     if (e != hipSuccess) return hip_fail(e, "convert launch");
   }
   return ok();
@@ -861,6 +1086,38 @@ int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream_ptr)
     e = launch_lds(asr::stream_copy, grid, lds, stream, static_cast<const asr::u32x4*>(src),
                    static_cast<asr::u32x4*>(dst), n16, slot0);
     if (e != hipSuccess) return hip_fail(e, "copy launch");
+  }
+  return ok();
+}
+
+int asr_hbm_probe(int32_t kind, void* dst, const void* src, int64_t bytes, void* stream_ptr) {
+  if (kind == ASR_PROBE_COPY) return asr_stream_copy(dst, src, bytes, stream_ptr);
+  if (kind != ASR_PROBE_READ && kind != ASR_PROBE_WRITE)
+    return fail(ASR_EINVAL, "kind must be ASR_PROBE_READ, ASR_PROBE_WRITE or ASR_PROBE_COPY");
+  if (bytes < 0) return fail(ASR_EINVAL, "bytes < 0");
+  if (bytes == 0) return ok();
+  const void* buf = kind == ASR_PROBE_READ ? src : dst;
+  if (!buf || (kind == ASR_PROBE_READ && !dst)) return fail(ASR_EINVAL, "NULL buffer");
+  if (bytes % 16 != 0 || !aligned(buf, 16) || !aligned(dst, 16))
+    return fail(ASR_EALIGN, "buffers and size must be multiples of 16 bytes");
+  const uint64_t n16 = static_cast<uint64_t>(bytes) / 16;
+  const uint64_t per_slot = static_cast<uint64_t>(asr::kBlock) * asr::kCopyVec;
+  const uint64_t n_slots = (n16 + per_slot - 1) / per_slot;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const void* k = kind == ASR_PROBE_READ ? reinterpret_cast<const void*>(asr::stream_read)
+                                         : reinterpret_cast<const void*>(asr::stream_write);
+  uint32_t lds = 0;
+  hipError_t e = occupancy_lds(k, &lds);
+  if (e != hipSuccess) return hip_fail(e, "probe attribute");
+  for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
+    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
+    if (kind == ASR_PROBE_READ)
+      e = launch_lds(asr::stream_read, grid, lds, stream, static_cast<const asr::u32x4*>(src),
+                     static_cast<asr::u32x4*>(dst), n16, slot0);
+    else
+      e = launch_lds(asr::stream_write, grid, lds, stream, static_cast<asr::u32x4*>(dst), n16,
+                     slot0, 0x3F803F80u);
+    if (e != hipSuccess) return hip_fail(e, "probe launch");
   }
   return ok();
 }

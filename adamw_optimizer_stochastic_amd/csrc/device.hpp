@@ -65,6 +65,8 @@ __device__ __forceinline__ Words4 stream_call(uint64_t j, uint32_t seed,
                        0u, 0u, seed, step);
 }
 
+constexpr uint64_t kCounterMask = (uint64_t{1} << 62) - 1;
+
 // 16 random bits for the V consecutive positions pos0 .. pos0+V-1, where
 // PHASE = pos0 & 3 is known at compile time. Position pos0+e takes word
 // (PHASE+e) & 3 of call (pos0 >> 2) + ((PHASE+e) >> 2): V/4 calls when the
@@ -77,7 +79,10 @@ __device__ __forceinline__ void stream_bits(uint64_t pos0, uint32_t seed, uint32
   uint32_t words[4 * kCalls];
 #pragma unroll
   for (int k = 0; k < kCalls; ++k) {
-    const Words4 w = stream_call(j0 + k, seed, step);
+    // Positions wrap modulo 2**64, so their counters p >> 2 wrap modulo
+    // 2**62: a run that crosses 2**64 continues at counter 0.
+    const uint64_t j = k == 0 ? j0 : ((j0 + k) & kCounterMask);
+    const Words4 w = stream_call(j, seed, step);
 #pragma unroll
     for (int q = 0; q < 4; ++q) words[4 * k + q] = w.w[q];
   }
@@ -227,32 +232,39 @@ __device__ __forceinline__ void store_vec_bf16(uint16_t* dst, const uint32_t (&h
   }
 }
 
-// Element-wise forms for the ragged tail and for unaligned tensors: only
-// elements e < count are touched.
+// Element-wise forms for a run that is cut by either end of its tensor, or
+// whose buffers are not vector-aligned: element e of the run is element
+// i0 + e of the buffer, and only lo <= e < hi is touched (i0 is negative for
+// the first run of a tensor whose runs start before it, see the kernels).
 template <int V>
-__device__ __forceinline__ void load_n(const float* src, int count, float (&x)[V]) {
+__device__ __forceinline__ void load_range(const float* base, int64_t i0, int lo, int hi,
+                                           float (&x)[V]) {
 #pragma unroll
-  for (int e = 0; e < V; ++e) x[e] = (e < count) ? src[e] : 0.0f;
+  for (int e = 0; e < V; ++e) x[e] = (e >= lo && e < hi) ? base[i0 + e] : 0.0f;
 }
 
 template <int V>
-__device__ __forceinline__ void load_n(const uint16_t* src, int count, float (&x)[V]) {
-#pragma unroll
-  for (int e = 0; e < V; ++e) x[e] = (e < count) ? bf16_bits_to_f32(src[e]) : 0.0f;
-}
-
-template <int V>
-__device__ __forceinline__ void store_n(float* dst, int count, const float (&x)[V]) {
+__device__ __forceinline__ void load_range(const uint16_t* base, int64_t i0, int lo, int hi,
+                                           float (&x)[V]) {
 #pragma unroll
   for (int e = 0; e < V; ++e)
-    if (e < count) dst[e] = x[e];
+    x[e] = (e >= lo && e < hi) ? bf16_bits_to_f32(base[i0 + e]) : 0.0f;
 }
 
 template <int V>
-__device__ __forceinline__ void store_n_bf16(uint16_t* dst, int count, const uint32_t (&h)[V]) {
+__device__ __forceinline__ void store_range(float* base, int64_t i0, int lo, int hi,
+                                            const float (&x)[V]) {
 #pragma unroll
   for (int e = 0; e < V; ++e)
-    if (e < count) dst[e] = static_cast<uint16_t>(h[e]);
+    if (e >= lo && e < hi) base[i0 + e] = x[e];
+}
+
+template <int V>
+__device__ __forceinline__ void store_range_bf16(uint16_t* base, int64_t i0, int lo, int hi,
+                                                 const uint32_t (&h)[V]) {
+#pragma unroll
+  for (int e = 0; e < V; ++e)
+    if (e >= lo && e < hi) base[i0 + e] = static_cast<uint16_t>(h[e]);
 }
 
 }  // namespace asr

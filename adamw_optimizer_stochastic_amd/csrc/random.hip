@@ -63,7 +63,12 @@ struct Params {
   float a, b;          // uniform: low, high - low; normal: mean, std; dropout: scale
   uint32_t threshold;  // dropout
   uint32_t seed, step;
-  uint32_t vec_ok;     // x and y aligned for 4-element vector access
+  // Runs of 4 positions start `shift` elements before element 0 (the first
+  // run's leading lanes touch nothing), so that whole runs are vector-
+  // aligned in x and y; vec_ok says such a shift exists (else shift is 0
+  // and every element moves on its own).
+  uint32_t vec_ok;
+  uint32_t shift;
 };
 
 // Words of positions (p0 & ~3) + k, k < 4 (PHASE == 0) or k < 8.
@@ -75,7 +80,8 @@ __device__ __forceinline__ void run_words(uint64_t p0, uint32_t seed, uint32_t s
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = a.w[k];
   if constexpr (PHASE > 0) {
-    const asr::Words4 b = asr::stream_call(j0 + 1, seed, step);
+    // a run that crosses position 2**64 continues at counter 0
+    const asr::Words4 b = asr::stream_call((j0 + 1) & asr::kCounterMask, seed, step);
 #pragma unroll
     for (int k = 0; k < 4; ++k) w[4 + k] = b.w[k];
   } else {
@@ -114,29 +120,34 @@ box_muller_given_words(const uint32_t* __restrict__ w_even, const uint32_t* __re
     box_muller(w_even[i], w_odd[i], zc[i], zs[i]);
 }
 
+// Elements i0 + e of a buffer, for the e in [lo, hi) that lie inside it.
 template <typename T>
-__device__ __forceinline__ void load4(const T* src, bool full, int count, float (&x)[4]) {
-  if (full) asr::load_vec<false, 4>(src, x);
-  else asr::load_n(src, count, x);
+__device__ __forceinline__ void load4(const T* base, int64_t i0, bool full, int lo, int hi,
+                                      float (&x)[4]) {
+  if (full) asr::load_vec<false, 4>(base + i0, x);
+  else asr::load_range(base, i0, lo, hi, x);
 }
 
-__device__ __forceinline__ void store4(float* dst, bool full, int count, const float (&y)[4]) {
-  if (full) asr::store_vec<false, 4>(dst, y);
-  else asr::store_n(dst, count, y);
+__device__ __forceinline__ void store4(float* base, int64_t i0, bool full, int lo, int hi,
+                                       const float (&y)[4]) {
+  if (full) asr::store_vec<false, 4>(base + i0, y);
+  else asr::store_range(base, i0, lo, hi, y);
 }
 
-__device__ __forceinline__ void store4(uint16_t* dst, bool full, int count, const float (&y)[4]) {
+__device__ __forceinline__ void store4(uint16_t* base, int64_t i0, bool full, int lo, int hi,
+                                       const float (&y)[4]) {
   uint32_t h[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) h[e] = asr::round_rn(__float_as_uint(y[e]));
-  if (full) asr::store_vec_bf16<false, 4>(dst, h);
-  else asr::store_n_bf16(dst, count, h);
+  if (full) asr::store_vec_bf16<false, 4>(base + i0, h);
+  else asr::store_range_bf16(base, i0, lo, hi, h);
 }
 
-// One lane: positions p0 .. p0 + 3 (count of them inside the tensor).
+// One lane: positions of elements i0 .. i0 + 3, of which lo <= e < hi lie
+// inside the tensor.
 template <int OP, typename T, int PHASE>
-__device__ __forceinline__ void run(const Params& P, int64_t i0, int count) {
-  const bool full = P.vec_ok && count == kVec;
+__device__ __forceinline__ void run(const Params& P, int64_t i0, int lo, int hi) {
+  const bool full = P.vec_ok && lo == 0 && hi == kVec;
   const uint64_t p0 = P.base_index + static_cast<uint64_t>(i0);
   uint32_t w[8];
   run_words<PHASE>(p0, P.seed, P.step, w);
@@ -154,7 +165,7 @@ __device__ __forceinline__ void run(const Params& P, int64_t i0, int count) {
     for (int e = 0; e < 4; ++e) y[e] = P.a + P.b * z[PHASE + e];
   } else {
     float x[4];
-    load4(static_cast<const T*>(P.x) + i0, full, count, x);
+    load4(static_cast<const T*>(P.x), i0, full, lo, hi, x);
     uint32_t keep = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -163,31 +174,32 @@ __device__ __forceinline__ void run(const Params& P, int64_t i0, int count) {
       y[e] = x[e] * (k ? P.a : 0.0f);
     }
     if (P.mask) {
-      uint8_t* m = P.mask + i0;
-      if (count == kVec && (reinterpret_cast<uintptr_t>(m) & 3) == 0) {
-        *reinterpret_cast<uint32_t*>(m) = keep;
+      if (lo == 0 && hi == kVec && ((reinterpret_cast<uintptr_t>(P.mask) + i0) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(P.mask + i0) = keep;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (e < count) m[e] = static_cast<uint8_t>((keep >> (8 * e)) & 1u);
+          if (e >= lo && e < hi) P.mask[i0 + e] = static_cast<uint8_t>((keep >> (8 * e)) & 1u);
       }
     }
   }
-  store4(static_cast<T*>(P.y) + i0, full, count, y);
+  store4(static_cast<T*>(P.y), i0, full, lo, hi, y);
 }
 
 template <int OP, typename T>
 __global__ void __launch_bounds__(kBlock) rng_kernel(Params P) {
   const int64_t i0 = static_cast<int64_t>(P.slot0 + slot_of_block(blockIdx.x, gridDim.x)) * kSlot +
-                     static_cast<int64_t>(threadIdx.x) * kVec;
+                     static_cast<int64_t>(threadIdx.x) * kVec - static_cast<int64_t>(P.shift);
   const int64_t left = P.n - i0;
   if (left <= 0) return;
-  const int count = left < kVec ? static_cast<int>(left) : kVec;
-  switch (static_cast<int>(P.base_index & 3u)) {
-    case 0: run<OP, T, 0>(P, i0, count); break;
-    case 1: run<OP, T, 1>(P, i0, count); break;
-    case 2: run<OP, T, 2>(P, i0, count); break;
-    default: run<OP, T, 3>(P, i0, count); break;
+  const int hi = left < kVec ? static_cast<int>(left) : kVec;
+  const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
+  // every run of the tensor starts at the same phase within its Philox call
+  switch (static_cast<int>((P.base_index - P.shift) & 3u)) {
+    case 0: run<OP, T, 0>(P, i0, lo, hi); break;
+    case 1: run<OP, T, 1>(P, i0, lo, hi); break;
+    case 2: run<OP, T, 2>(P, i0, lo, hi); break;
+    default: run<OP, T, 3>(P, i0, lo, hi); break;
   }
 }
 
@@ -206,7 +218,8 @@ bool aligned_to(const void* p, uintptr_t a) {
 
 template <int OP, typename T>
 hipError_t launch_all(asr_rng::Params P, hipStream_t stream) {
-  const uint64_t n_slots = (static_cast<uint64_t>(P.n) + asr_rng::kSlot - 1) / asr_rng::kSlot;
+  const uint64_t n_slots =
+      (static_cast<uint64_t>(P.n) + P.shift + asr_rng::kSlot - 1) / asr_rng::kSlot;
   for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr_rng::kMaxGrid) {
     P.slot0 = slot0;
     const uint32_t grid =
@@ -238,6 +251,25 @@ int check_common(const void* y, int32_t dtype, int64_t n) {
 
 uint32_t vec_alignment(int32_t dtype) { return dtype == ASR_F32 ? 16 : 8; }
 
+// Sets P.shift to the s in [0, 4) for which elements 4k - s of x (if
+// given) and y sit on vector-aligned addresses, and P.vec_ok to whether
+// there is one. A piece cut from aligned buffers at element offset o has
+// s = o mod 4.
+void choose_shift(asr_rng::Params& P, int32_t dtype) {
+  const uintptr_t elem = dtype == ASR_F32 ? 4 : 2, vec = vec_alignment(dtype);
+  P.vec_ok = 0;
+  P.shift = 0;
+  for (uint32_t s = 0; s < 4; ++s) {
+    const bool y_ok = ((reinterpret_cast<uintptr_t>(P.y) + (4 - s) * elem) & (vec - 1)) == 0;
+    const bool x_ok = !P.x || ((reinterpret_cast<uintptr_t>(P.x) + (4 - s) * elem) & (vec - 1)) == 0;
+    if (y_ok && x_ok) {
+      P.vec_ok = 1;
+      P.shift = s;
+      return;
+    }
+  }
+}
+
 // The draws are formed in binary32: a parameter must be a finite binary32 value.
 bool fits_f32(double v) { return std::isfinite(v) && std::fabs(v) <= 3.4028234663852886e38; }
 
@@ -259,7 +291,7 @@ int asr_random_uniform(void* out, int32_t dtype, int64_t n, double low, double h
   P.b = static_cast<float>(high - low);
   P.seed = seed;
   P.step = step;
-  P.vec_ok = aligned_to(out, vec_alignment(dtype));
+  choose_shift(P, dtype);
   return dispatch<asr_rng::kUniform>(P, dtype, static_cast<hipStream_t>(stream), "uniform launch");
 }
 
@@ -277,7 +309,7 @@ int asr_random_normal(void* out, int32_t dtype, int64_t n, double mean, double s
   P.b = static_cast<float>(std);
   P.seed = seed;
   P.step = step;
-  P.vec_ok = aligned_to(out, vec_alignment(dtype));
+  choose_shift(P, dtype);
   return dispatch<asr_rng::kNormal>(P, dtype, static_cast<hipStream_t>(stream), "normal launch");
 }
 
@@ -298,7 +330,7 @@ int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype, int64_t n,
   P.threshold = static_cast<uint32_t>(std::min(std::floor(p * 4294967296.0), 4294967295.0));
   P.seed = seed;
   P.step = step;
-  P.vec_ok = aligned_to(x, vec_alignment(dtype)) && aligned_to(y, vec_alignment(dtype));
+  choose_shift(P, dtype);
   return dispatch<asr_rng::kDropout>(P, dtype, static_cast<hipStream_t>(stream), "dropout launch");
 }
 

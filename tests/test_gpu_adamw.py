@@ -126,25 +126,100 @@ def test_mixed_dtype_list_one_call():
         _check_outputs(dev[k][:1] + dev[k][2:], want, pdt, f"tensor {k}")
 
 
-@pytest.mark.parametrize("offset", [1, 2, 3, 5])
-def test_unaligned_views_take_elementwise_path(offset):
-    """Views starting `offset` elements into their storage are not 16-byte
-    aligned; results must not change."""
-    announce("unaligned views", offset)
-    n = 10000
-    rng = wl.host_rng(wl.CFG_SMALL, 50 + offset, 0)
-    p = _host_tensor(rng, n + offset, BF16, 0.02)
-    g = _host_tensor(rng, n + offset, BF16, 1e-3)
-    m = wl.normal_f32(rng, n + offset, 1e-4)
-    v = np.abs(wl.normal_f32(rng, n + offset, 1e-7))
-    pd, gd, md, vd = bf16_tensor(p), bf16_tensor(g), f32_tensor(m), f32_tensor(v)
+_OFFSETS = [(1, 1, 1, 1), (2, 2, 2, 2), (3, 3, 3, 3), (5, 5, 5, 5), (6, 6, 6, 6), (7, 7, 7, 7),
+            (1, 2, 3, 1), (0, 4, 2, 6)]
+
+
+@pytest.mark.parametrize("n", [3, 10000])
+@pytest.mark.parametrize("offsets", _OFFSETS, ids=lambda o: "-".join(map(str, o)))
+@pytest.mark.parametrize("pdt,gdt", [(BF16, BF16), (F32, F32), (BF16, F32), (F32, BF16)])
+def test_unaligned_views_with_guards(pdt, gdt, offsets, n):
+    """Views that start `offsets` (param, grad, m, v) elements into their
+    storage and end 5 elements before its end. Equal offsets (a piece cut
+    from aligned buffers) keep the vector path with shifted runs; unequal
+    ones go element by element. Results equal the oracle's, and the head and
+    tail outside each view are not written."""
+    announce("unaligned views", pdt, gdt, offsets, n)
+    tail = 5
+    rng = wl.host_rng(wl.CFG_SMALL, 50 + sum(offsets), n)
+    op, og, om, ov = offsets
+    p = _host_tensor(rng, op + n + tail, pdt, 0.02)
+    g = _host_tensor(rng, og + n + tail, gdt, 1e-3)
+    m = wl.normal_f32(rng, om + n + tail, 1e-4)
+    v = np.abs(wl.normal_f32(rng, ov + n + tail, 1e-7))
+    pd, gd, md, vd = _to_dev(p, pdt), _to_dev(g, gdt), f32_tensor(m), f32_tensor(v)
     base = 1001
-    ops.adamw_step([pd[offset:]], [gd[offset:]], [md[offset:]], [vd[offset:]], [base], step=5,
-                   seed=4, **HP)
-    want = oracle.step_tensor(p[offset:], g[offset:], m[offset:], v[offset:], param_dtype=BF16,
-                              grad_dtype=BF16, base_index=base, step=5, seed=4, **HP)
-    _check_outputs((pd[offset:], md[offset:], vd[offset:]), want, BF16, "unaligned")
-    assert_bits_equal(to_host(pd[:offset]), p[:offset], "untouched head")
+    for rmode, rounding in (("sr", ROUND_SR), ("rn", ROUND_RN)):
+        pd.copy_(_to_dev(p, pdt))
+        md.copy_(f32_tensor(m))
+        vd.copy_(f32_tensor(v))
+        ops.adamw_step([pd[op:op + n]], [gd[og:og + n]], [md[om:om + n]], [vd[ov:ov + n]],
+                       [base], step=5, seed=4, rounding=rmode, **HP)
+        want = oracle.step_tensor(p[op:op + n], g[og:og + n], m[om:om + n], v[ov:ov + n],
+                                  param_dtype=pdt, grad_dtype=gdt, base_index=base, step=5,
+                                  seed=4, rounding=rounding, **HP)
+        _check_outputs((pd[op:op + n], md[om:om + n], vd[ov:ov + n]), want, pdt,
+                       f"unaligned {rmode}")
+        for dev_t, host, off, name in ((pd, p, op, "param"), (md, m, om, "m"), (vd, v, ov, "v")):
+            assert_bits_equal(to_host(dev_t[:off]), host[:off], f"{name} head")
+            assert_bits_equal(to_host(dev_t[off + n:]), host[off + n:], f"{name} tail")
+
+
+@pytest.mark.parametrize("base", [(1 << 64) - 3, (1 << 64) - 4098, (1 << 64) - 1])
+def test_positions_wrap_past_2pow64(base):
+    """Global positions wrap modulo 2**64, and so do their Philox counters
+    (modulo 2**62): a tensor whose positions cross 2**64 -- with a run of
+    four that straddles it, aligned and shifted -- matches the oracle."""
+    announce("positions wrap", base)
+    n = 9000
+    rng = wl.host_rng(wl.CFG_SMALL, 60, base & 0xFFFF)
+    p = _host_tensor(rng, n + 1, BF16, 0.02)
+    g = _host_tensor(rng, n + 1, BF16, 1e-3)
+    for off in (0, 1):
+        pd, gd = bf16_tensor(p), bf16_tensor(g)
+        md = torch.zeros(n + 1, dtype=torch.float32, device="cuda")
+        vd = torch.zeros(n + 1, dtype=torch.float32, device="cuda")
+        ops.adamw_step([pd[off:off + n]], [gd[off:off + n]], [md[off:off + n]],
+                       [vd[off:off + n]], [base], step=2, seed=11, **HP)
+        z = np.zeros(n, np.float32)
+        want = oracle.step_tensor(p[off:off + n], g[off:off + n], z, z, param_dtype=BF16,
+                                  grad_dtype=BF16, base_index=base, step=2, seed=11, **HP)
+        _check_outputs((pd[off:off + n], md[off:off + n], vd[off:off + n]), want, BF16,
+                       f"wrap base {base} offset {off}")
+
+
+@pytest.mark.parametrize("pdt,gdt,rounding", [
+    (F32, F32, ROUND_SR), (F32, BF16, ROUND_SR), (BF16, F32, ROUND_SR), (BF16, F32, ROUND_RN),
+    (BF16, BF16, ROUND_RN), (BF16, BF16, ROUND_SR)])
+def test_size_class_launch_every_dtype_pair(pdt, gdt, rounding):
+    """Two tensors of 1,048,579 elements (1,025 slots of 1,024 each, 2,050
+    in all: a size-class launch, not the slot table) for every dtype pair
+    and rounding, one of them a view three elements into its storage (its
+    runs shifted by three, still 1,025 slots), odd base indices, two steps,
+    checked in full against the oracle."""
+    announce("size-class launch", pdt, gdt, rounding)
+    n, off = 1_048_579, 3
+    rng = wl.host_rng(wl.CFG_SMALL, 70 + 4 * pdt + 2 * gdt + rounding, 0)
+    bases = [(1 << 33) + 5, (1 << 33) + 5 + n]
+    rmode = "sr" if rounding == ROUND_SR else "rn"
+    host, dev = [], []
+    for k in range(2):
+        o = off if k == 1 else 0
+        p = _host_tensor(rng, n + o, pdt, 0.02)
+        m = wl.normal_f32(rng, n + o, 1e-4)
+        v = np.abs(wl.normal_f32(rng, n + o, 1e-7))
+        host.append([p[o:], m[o:], v[o:]])
+        dev.append([_to_dev(p, pdt)[o:], f32_tensor(m)[o:], f32_tensor(v)[o:]])
+    for t in (1, 2):
+        gh = [_host_tensor(rng, n, gdt, 1e-3) for _ in range(2)]
+        ops.adamw_step([d[0] for d in dev], [_to_dev(x, gdt) for x in gh], [d[1] for d in dev],
+                       [d[2] for d in dev], bases, step=t, seed=13, rounding=rmode, **HP)
+        for k in range(2):
+            host[k] = list(oracle.step_tensor(*host[k][:1], gh[k], *host[k][1:],
+                                              param_dtype=pdt, grad_dtype=gdt,
+                                              base_index=bases[k], step=t, seed=13,
+                                              rounding=rounding, **HP))
+            _check_outputs(dev[k], host[k], pdt, f"tensor {k} step {t}")
 
 
 def test_extreme_values_nan_inf_subnormal():

@@ -49,7 +49,7 @@ def test_philox_fill_unaligned_output():
 
 # ------------------------------------------------------------ conversions
 SIZES = [1, 3, 8, 9, 2047, 2048, 2053, (1 << 20) + 13]
-BASES = [0, 1, 3, 5, (1 << 32) - 3, (1 << 32) + 5, (1 << 34) - 3, (1 << 34) + 5]
+BASES = [0, 1, 3, 5, (1 << 32) - 3, (1 << 32) + 5, (1 << 34) - 3, (1 << 34) + 5, (1 << 64) - 3]
 
 
 def _convert_input(n, seed):
@@ -80,17 +80,26 @@ def test_cvt_rn_bit_exact(n):
     assert_bits_equal(got, oracle.cvt_f32_bf16_rn(x), "cvt rn")
 
 
-@pytest.mark.parametrize("offset_in,offset_out", [(1, 0), (0, 1), (3, 5)])
+@pytest.mark.parametrize("offset_in,offset_out", [(1, 0), (0, 1), (3, 5), (1, 1), (4, 4),
+                                                (5, 5), (2, 6), (7, 7)])
 def test_cvt_unaligned_views(offset_in, offset_out):
+    """Views that start inside their storage and end 3 elements before its
+    end. Offsets that leave both buffers equally misaligned modulo a vector
+    (a piece cut from aligned buffers) keep the vector path with shifted
+    runs; others go element by element. Nothing outside the output view is
+    written."""
     announce("cvt unaligned", offset_in, offset_out)
-    n = 5000
-    x = _convert_input(n + offset_in, 3)
-    xin = f32_tensor(x)[offset_in:]
-    out_buf = torch.zeros(n + offset_out, dtype=torch.bfloat16, device="cuda")
-    ops.cvt_f32_bf16_sr(xin, 11, 4, 33, out=out_buf[offset_out:])
-    got = to_host(out_buf)
-    assert np.all(got[:offset_out] == 0)
-    assert_bits_equal(got[offset_out:], oracle.cvt_f32_bf16_sr(x[offset_in:], 11, 4, 33), "cvt")
+    n, tail = 5000, 3
+    x = _convert_input(n + offset_in + tail, 3)
+    xin = f32_tensor(x)[offset_in:offset_in + n]
+    out_buf = torch.zeros(n + offset_out + tail, dtype=torch.bfloat16, device="cuda")
+    for base in (33, (1 << 64) - 2):
+        out_buf.zero_()
+        ops.cvt_f32_bf16_sr(xin, 11, 4, base, out=out_buf[offset_out:offset_out + n])
+        got = to_host(out_buf)
+        assert np.all(got[:offset_out] == 0) and np.all(got[offset_out + n:] == 0)
+        assert_bits_equal(got[offset_out:offset_out + n],
+                          oracle.cvt_f32_bf16_sr(x[offset_in:offset_in + n], 11, 4, base), "cvt")
 
 
 def test_cvt_sr_seed_and_step_change_bits():

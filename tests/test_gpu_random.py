@@ -211,3 +211,44 @@ def test_full_size_sampled():
         wy, wk = orng.dropout_f32(xi[k:k + 1], 0.1, 2, 0, int(i))
         assert yi[k].view(np.uint32) == wy[0].view(np.uint32) and bool(mi[k]) == bool(wk[0])
     del x, y, mask
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3, 6])
+@pytest.mark.parametrize("base", [7, (1 << 64) - 3])
+def test_unaligned_views_and_wrap_with_guards(offset, base):
+    """Dropout (with mask) and uniform fills into views that start `offset`
+    elements into their storage and end 3 before its end, f32 and bf16;
+    positions that cross 2**64. Bit-exact against the oracle, and nothing
+    outside the views is written."""
+    from adamw_optimizer_stochastic_amd import _abi
+    announce("rng unaligned", offset, base)
+    n, tail, seed, step, p = 5000, 3, 17, 3, 0.3
+    total = n + offset + tail
+    stream = torch.cuda.current_stream().cuda_stream
+    x = np.random.default_rng(offset).standard_normal(total).astype(np.float32)
+    for dtype, code in ((torch.float32, _abi.ASR_F32), (torch.bfloat16, _abi.ASR_BF16)):
+        if dtype == torch.float32:
+            xd, xs = f32_tensor(x), x[offset:offset + n]
+        else:
+            xb = oracle.rn_bf16(oracle.f32_bits(x)).astype(np.uint16)
+            xd, xs = bf16_tensor(xb), xb[offset:offset + n]
+        y = torch.zeros(total, dtype=dtype, device="cuda")
+        mk = torch.full((total,), 7, dtype=torch.uint8, device="cuda")
+        _abi.asr_dropout(xd[offset:].data_ptr(), y[offset:].data_ptr(), mk[offset:].data_ptr(),
+                         code, n, p, seed, step, base, stream)
+        wy, wk = (orng.dropout_f32 if code == _abi.ASR_F32 else orng.dropout_bf16)(
+            xs, p, seed, step, base)
+        gy, gm = to_host(y), to_host(mk)
+        assert_bits_equal(gy[offset:offset + n], wy, f"dropout {dtype}")
+        assert np.array_equal(gm[offset:offset + n].astype(bool), wk)
+        assert not gy[:offset].any() and not gy[offset + n:].any()
+        assert np.all(gm[:offset] == 7) and np.all(gm[offset + n:] == 7)
+        u = torch.zeros(total, dtype=dtype, device="cuda")
+        _abi.asr_random_uniform(u[offset:].data_ptr(), code, n, -1.0, 2.0, seed, step, base,
+                                stream)
+        wu = orng.uniform_f32(n, seed, step, base, -1.0, 2.0)
+        if code == _abi.ASR_BF16:
+            wu = oracle.rn_bf16(oracle.f32_bits(wu))
+        gu = to_host(u)
+        assert_bits_equal(gu[offset:offset + n], wu, f"uniform {dtype}")
+        assert not gu[:offset].any() and not gu[offset + n:].any()
