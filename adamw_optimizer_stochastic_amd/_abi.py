@@ -16,7 +16,8 @@ from ._build import LIB_PATH
 ASR_OK, ASR_EINVAL, ASR_EDTYPE, ASR_EALIGN, ASR_EWORKSPACE, ASR_EHIP = range(6)
 ASR_F32, ASR_BF16 = 0, 1
 ASR_ROUND_SR, ASR_ROUND_RN = 0, 1
-ABI_VERSION = 105
+ASR_PROBE_READ, ASR_PROBE_WRITE, ASR_PROBE_COPY = 0, 1, 2
+ABI_VERSION = 106
 
 STATUS_NAMES = {ASR_OK: "ASR_OK", ASR_EINVAL: "ASR_EINVAL", ASR_EDTYPE: "ASR_EDTYPE",
                 ASR_EALIGN: "ASR_EALIGN", ASR_EWORKSPACE: "ASR_EWORKSPACE",
@@ -69,6 +70,9 @@ _SIGNATURES = {
                                _c.c_void_p]),
     "asr_box_muller_given_words": (_c.c_int, [_c.c_void_p] * 4 + [_c.c_int64, _c.c_void_p]),
     "asr_stream_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "asr_hbm_probe": (_c.c_int, [_c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "asr_adamw_stream_probe": (_c.c_int, [_c.POINTER(AsrTensor), _c.c_int32, _c.c_void_p,
+                                          _c.c_size_t, _c.c_void_p]),
     "asr_gemm_bf16": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                  _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
                                  _c.c_int32, _c.c_uint32, _c.c_uint32, _c.c_uint64,
@@ -196,3 +200,14 @@ def asr_stream_copy(dst, src, nbytes, stream):
 
 def asr_sr_bf16_given_bits(x, r16, out, n, stream):
     _check(lib().asr_sr_bf16_given_bits(x, r16, out, n, stream), "asr_sr_bf16_given_bits")
+
+
+def asr_hbm_probe(kind, dst, src, nbytes, stream):
+    _check(lib().asr_hbm_probe(kind, dst, src, nbytes, stream), "asr_hbm_probe")
+
+
+def asr_adamw_stream_probe(tensors, workspace, workspace_bytes, stream):
+    """tensors: sequence of AsrTensor (or dicts); destroys the params."""
+    arr, n = _tensor_array(tensors)
+    _check(lib().asr_adamw_stream_probe(arr if n else None, n, workspace, workspace_bytes,
+                                        stream), "asr_adamw_stream_probe")

@@ -9,13 +9,17 @@ peak (algorithmic bytes: 22 per element), and the CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload llama3_8b|llama3_8b_rank|shards|convert|gemm|rng]
+                    [--workload llama3_8b|llama3_8b_rank|shards|convert|gemm|rng|hbm_probe]
     python bench.py --copy-probe      # plain copy of known size (counter scaling)
 
 The llama3_8b_rank workload is one data-parallel rank's share of the same
 list: the flattened list split into --ranks equal contiguous ranges
 (ZeRO-1), rank --rank's pieces (default 3 of 8: 42 pieces, cut at both
 ends), each with its global base_index.
+
+The hbm_probe workload measures what HBM gives the step's launch structure
+without the step's arithmetic: read-only, write-only and copy streams, and
+the Llama-3-8B list's own 4-read/3-write traffic timed against the step.
 
 The gemm workload times the bf16 GEMM with the SR epilogue on the gate/up
 projection of one Llama-3-8B MLP over 8,192 tokens (M=8192, N=14336,
@@ -93,13 +97,29 @@ def _oracle_shard(args):
     return time.perf_counter() - t0
 
 
+# Worker processes for the CPU baseline: the CPUs this process may run on,
+# at most 16 -- the host share of one GPU on the MI355X machines this runs
+# on, whatever larger count the host reports.
+HOST_SHARE_CPUS = 16
+
+
+def host_cpus():
+    """(cpus this process may run on, cpus the host reports)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return usable, os.cpu_count() or usable
+
+
 def cpu_baseline(per_core=1 << 22):
     """The oracle (numpy, unmodified) on `cores` shards of `per_core` bf16
     elements each, one process per core, before the GPU is touched (the pool
     forks a process that has not initialised the GPU). Each shard times its
     own step (input generation excluded); the shards run concurrently, so
     the whole-host rate is the sum of the per-core rates."""
-    cores = max(1, min(16, os.cpu_count() or 1))
+    usable, reported = host_cpus()
+    cores = max(1, min(HOST_SHARE_CPUS, usable))
     ctx = multiprocessing.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(cores) as pool:
@@ -108,6 +128,10 @@ def cpu_baseline(per_core=1 << 22):
     rates = sorted(per_core / t for t in times)
     n = cores * per_core
     return {"value": sum(rates), "unit": "params/s", "cores": cores, "kind": "oracle",
+            "host_cpu_count": reported, "usable_cpus": usable,
+            "cores_note": f"one process per core on {cores} cores: the host share of one GPU "
+                          f"(at most {HOST_SHARE_CPUS}); the host reports {reported} CPUs, "
+                          f"{usable} usable by this process",
             "one_core_value": rates[len(rates) // 2],
             "sample": f"{n} bf16 params ({cores} concurrent shards of {per_core}) of the same "
                       f"workload, one AdamW-SR step each, numpy oracle; step times "
@@ -179,6 +203,12 @@ def run_adamw(args, torch, ops, wl):
                       exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=dev),
                       base_index=0)]
         cfg_name = "single_tensor_268M"
+        if args.odd_split:
+            # two pieces cut at an odd element: the second piece's buffers all
+            # start 1 element past a 16-byte boundary (shifted runs)
+            state = odd_split(state[0], SHARDS_ODD_CUT)
+            cfg_name = "single_tensor_268M_odd_split"
+            extra = {"pieces": [[0, SHARDS_ODD_CUT], [SHARDS_ODD_CUT, n]]}
     n_elems = sum(t["param"].numel() for t in state)
     lists = ([t["param"] for t in state], [t["grad"] for t in state],
              [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
@@ -210,8 +240,16 @@ def run_adamw(args, torch, ops, wl):
     bytes_per_launch = 22 * n_elems
     achieved = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(args.workload, n_elems)
+    # The same list's traffic without the arithmetic (after the timed steps:
+    # it overwrites the parameters), timed like the step.
+    probe_ms = adamw_stream_probe_ms(torch, state, ws, stream, args.steps)
+    probe_gbps = bytes_per_launch / (probe_ms * 1e-3) / 1e9
     copy_gbps = stream_copy_gbps(torch, dev, stream)
+    context = {}
+    if args.workload == "shards":
+        context = whole_vs_odd_split(torch, ops, state, ws, stream, args.steps)
     return {
+        "context": context,
         "metric": METRIC, "value": n_elems / (ms_per_step * 1e-3), "unit": "params/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -229,7 +267,11 @@ def run_adamw(args, torch, ops, wl):
                                "kernels of one step (metadata upload, slot table, step)",
                      "copy_GBps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
                      "copy_note": "asr_stream_copy, 2 x 8 GiB, a 1:1 copy built like the step "
-                                  "(same slots, 128-bit accesses, XCD windows, residency cap)"},
+                                  "(same slots, 128-bit accesses, XCD windows, residency cap)",
+                     "probe_GBps": probe_gbps, "frac_of_probe": achieved / probe_gbps,
+                     "probe_note": "asr_adamw_stream_probe on the same list: the step's launch "
+                                   "plan and accesses (4 streams read, 3 written) without its "
+                                   "arithmetic, same timing"},
     }
 
 
@@ -288,6 +330,72 @@ def stream_copy_gbps(torch, dev, stream, nbytes=8 << 30, reps=10):
     ms = s.elapsed_time(e) / reps
     del src, dst
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+SHARDS_ODD_CUT = 33554433
+
+
+def odd_split(t, cut):
+    """Two pieces [0, cut) and [cut, n) of one tensor's state, each with its
+    global base_index."""
+    n = t["param"].numel()
+    return [dict(name=f"{t['name']}[{a}:{b}]", param=t["param"][a:b], grad=t["grad"][a:b],
+                 exp_avg=t["exp_avg"][a:b], exp_avg_sq=t["exp_avg_sq"][a:b],
+                 base_index=t["base_index"] + a) for a, b in ((0, cut), (cut, n))]
+
+
+def whole_vs_odd_split(torch, ops, state, ws, stream, steps):
+    """The 268M-element tensor stepped whole and as two pieces cut at an odd
+    element, in three alternating blocks of `steps` calls each (HIP events
+    per call): the cost of a misaligned cut."""
+    pieces = state if len(state) == 2 else odd_split(state[0], SHARDS_ODD_CUT)
+    base = pieces[0]
+    # the two pieces are views of one storage: rebuild the whole views from it
+    n = sum(p["param"].numel() for p in pieces)
+    whole = [dict(name="w", base_index=base["base_index"],
+                  **{k: base[k].as_strided((n,), (1,)) for k in
+                     ("param", "grad", "exp_avg", "exp_avg_sq")})]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0,
+              rounding="sr", workspace=ws)
+    forms = {}
+    for name, st in (("whole", whole), ("odd_split", pieces)):
+        lists = ([t["param"] for t in st], [t["grad"] for t in st], [t["exp_avg"] for t in st],
+                 [t["exp_avg_sq"] for t in st], [t["base_index"] for t in st])
+        forms[name] = lists
+    ms = {"whole": [], "odd_split": []}
+    step = [1000]
+    for _ in range(3):
+        for name, lists in forms.items():
+            def fn(lists=lists):
+                step[0] += 1
+                ops.adamw_step(*lists, step=step[0], **hp)
+            fn()
+            ms[name].append(_time_launches(torch, stream, fn, steps)[1])
+    w, o = sum(ms["whole"]) / 3, sum(ms["odd_split"]) / 3
+    n_bytes = 22 * n
+    return {"whole_ms": w, "odd_split_ms": o, "whole_GBps": n_bytes / (w * 1e-3) / 1e9,
+            "odd_split_GBps": n_bytes / (o * 1e-3) / 1e9, "odd_split_over_whole_rate": w / o,
+            "blocks_ms": ms, "cut": SHARDS_ODD_CUT}
+
+
+def adamw_stream_probe_ms(torch, state, ws, stream, steps):
+    """Mean time of asr_adamw_stream_probe over the list (HIP events around
+    each call on the launch stream), after 2 untimed calls."""
+    from adamw_optimizer_stochastic_amd import _abi
+    descs = [_abi.AsrTensor(t["param"].data_ptr(), t["grad"].data_ptr(),
+                            t["exp_avg"].data_ptr(), t["exp_avg_sq"].data_ptr(),
+                            t["param"].numel(), t["base_index"],
+                            _abi.ASR_BF16 if t["param"].dtype == torch.bfloat16 else _abi.ASR_F32,
+                            _abi.ASR_BF16 if t["grad"].dtype == torch.bfloat16 else _abi.ASR_F32)
+             for t in state]
+    nbytes = ws.numel() * ws.element_size()
+
+    def fn():
+        _abi.asr_adamw_stream_probe(descs, ws.data_ptr(), nbytes, stream.cuda_stream)
+
+    for _ in range(2):
+        fn()
+    return _time_launches(torch, stream, fn, steps)[1]
 
 
 def _time_launches(torch, stream, fn, steps):
@@ -444,6 +552,81 @@ def run_rng(args, torch, ops, wl):
     }
 
 
+def run_hbm_probe(args, torch, ops, wl):
+    """What HBM gives the step's launch structure, without its arithmetic:
+    read-only, write-only and 1:1 copy streams (asr_hbm_probe, 16 GiB each
+    way), then the Llama-3-8B list's 4-read/3-write traffic
+    (asr_adamw_stream_probe) against the step itself, alternated in three
+    blocks so that drift during the run favours neither."""
+    from adamw_optimizer_stochastic_amd import _abi
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    nbytes = 16 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    simple = {}
+    for name, kind, moved in (("read", _abi.ASR_PROBE_READ, nbytes),
+                              ("write", _abi.ASR_PROBE_WRITE, nbytes),
+                              ("copy", _abi.ASR_PROBE_COPY, 2 * nbytes)):
+        def fn(kind=kind):
+            _abi.asr_hbm_probe(kind, dst.data_ptr(), src.data_ptr(), nbytes, s)
+        for _ in range(max(2, args.warmup)):
+            fn()
+        ms = _time_launches(torch, stream, fn, args.steps)[1]
+        simple[name] = {"bytes_per_launch": moved, "ms": ms,
+                        "GBps": moved / (ms * 1e-3) / 1e9}
+        print(f"[bench] hbm probe {name}: {simple[name]['GBps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+
+    state = wl.llama3_8b_state(dev, seed=0)
+    n_elems = sum(t["param"].numel() for t in state)
+    lists = ([t["param"] for t in state], [t["grad"] for t in state],
+             [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
+             [t["base_index"] for t in state])
+    ws = ops.make_workspace([t["param"].numel() for t in state], dev)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0,
+              rounding="sr", workspace=ws)
+    step = [0]
+
+    def adamw():
+        step[0] += 1
+        ops.adamw_step(*lists, step=step[0], **hp)
+
+    for _ in range(max(2, args.warmup)):
+        adamw()
+    bytes_per_launch = 22 * n_elems
+    step_ms, probe_ms = [], []
+    for _ in range(3):
+        step_ms.append(_time_launches(torch, stream, adamw, args.steps)[1])
+        probe_ms.append(adamw_stream_probe_ms(torch, state, ws, stream, args.steps))
+    st, pr = sum(step_ms) / 3, sum(probe_ms) / 3
+    step_gbps = bytes_per_launch / (st * 1e-3) / 1e9
+    probe_gbps = bytes_per_launch / (pr * 1e-3) / 1e9
+    return {
+        "metric": "HBM GB/s of the AdamW-SR step's access pattern without its arithmetic "
+                  "(4 streams read, 3 written), 1 GPU",
+        "value": probe_gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": pr, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "hbm_probe_llama3_8b_param_list", "params": n_elems,
+                   "algorithmic_bytes_per_param": 22, "simple_stream_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": probe_gbps, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": probe_gbps / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "stream_probe_class / stream_probe_slots (the step's launch "
+                               "plan, no arithmetic)", "kernel_ms_avg": pr},
+        "context": {"step_ms_blocks": step_ms, "probe_ms_blocks": probe_ms,
+                    "step_GBps": step_gbps, "step_over_probe": step_gbps / probe_gbps,
+                    "read_only": simple["read"], "write_only": simple["write"],
+                    "copy_1to1": simple["copy"],
+                    "timing": "HIP events on the launch stream around each call; step and "
+                              "probe alternated in 3 blocks of `steps` calls"},
+    }
+
+
 def run_copy_probe(args, torch):
     """A plain device copy of 8 GiB (torch's copy kernel), for scaling the
     FETCH_SIZE/WRITE_SIZE counters: it moves exactly 8 GiB each way."""
@@ -469,11 +652,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "llama3_8b_rank", "shards", "convert", "gemm", "rng"])
+                    choices=["llama3_8b", "llama3_8b_rank", "shards", "convert", "gemm", "rng",
+                             "hbm_probe"])
     ap.add_argument("--rank", type=int, default=3, help="rank whose share --workload "
                     "llama3_8b_rank times")
     ap.add_argument("--ranks", type=int, default=8)
     ap.add_argument("--gemm-shape", default=None, help="M,N,K for --workload gemm")
+    ap.add_argument("--odd-split", action="store_true", help="--workload shards: time the "
+                    "tensor as two pieces cut at an odd element")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -513,6 +699,8 @@ def main():
         res = run_gemm(args, torch, ops, wl)
     elif args.workload == "rng":
         res = run_rng(args, torch, ops, wl)
+    elif args.workload == "hbm_probe":
+        res = run_hbm_probe(args, torch, ops, wl)
     else:
         res = run_adamw(args, torch, ops, wl)
     if cpu is not None:

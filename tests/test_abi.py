@@ -224,3 +224,21 @@ def test_stream_copy_argument_errors():
     assert _status(f, 0x1000, 0x2000, 24, None) == E.ASR_EALIGN
     assert _status(f, 0x1008, 0x2000, 16, None) == E.ASR_EALIGN
     assert _status(f, 0, 0, 0, None) == E.ASR_OK
+
+
+def test_probe_argument_errors():
+    E = _abi
+    f = _abi.asr_hbm_probe
+    assert _status(f, 3, 0x1000, 0x2000, 16, None) == E.ASR_EINVAL
+    assert _status(f, E.ASR_PROBE_READ, 0x1000, 0x2000, -16, None) == E.ASR_EINVAL
+    assert _status(f, E.ASR_PROBE_READ, 0, 0x2000, 16, None) == E.ASR_EINVAL   # no sink
+    assert _status(f, E.ASR_PROBE_WRITE, 0, 0, 16, None) == E.ASR_EINVAL
+    assert _status(f, E.ASR_PROBE_WRITE, 0x1008, 0, 16, None) == E.ASR_EALIGN
+    assert _status(f, E.ASR_PROBE_WRITE, 0x1000, 0, 24, None) == E.ASR_EALIGN
+    assert _status(f, E.ASR_PROBE_COPY, 0x1000, 0x2008, 16, None) == E.ASR_EALIGN
+    assert _status(f, E.ASR_PROBE_READ, 0x1000, 0x2000, 0, None) == E.ASR_OK
+    g = _abi.asr_adamw_stream_probe
+    assert _status(g, [_t(numel=-1)], 0x10000, 1 << 20, None) == E.ASR_EINVAL
+    assert _status(g, [_t(param_dtype=5)], 0x10000, 1 << 20, None) == E.ASR_EDTYPE
+    assert _status(g, [_t()], 0, 1 << 20, None) == E.ASR_EWORKSPACE
+    assert _status(g, [], 0, 0, None) == E.ASR_OK

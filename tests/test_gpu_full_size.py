@@ -1,12 +1,16 @@
 """GPU parity at full size, in the launch configuration the benchmark times:
-  * the SR conversion of 2**30 f32 values with 0.1% +-Inf/NaN/FLT_MAX;
+  * the SR conversion of 2**30 f32 values with 0.1% +-Inf/NaN/FLT_MAX,
+    every output against the oracle;
+  * the f32 workload, 16,777,216 elements x 100 steps, bit-exact;
   * a 268,435,456-element bf16 step run whole, as 8 shards with their own
     base_index, and split at an odd element (adamw-sr page, Correctness:
     sharded and one-piece updates must agree bit for bit);
-  * one multi-tensor call over the whole Llama-3-8B-shaped list, and over
-    one data-parallel rank's share of it (pieces with global base_index).
-Outputs are checked bit for bit against the oracle on sampled windows and
-special positions, and by properties that hold at any size on the rest.
+  * one multi-tensor call over the whole Llama-3-8B-shaped list (layers 0
+    and 31 in full), and over one data-parallel rank's share of it (pieces
+    with global base_index).
+Outputs are checked bit for bit against the oracle, in full where the
+oracle can run over the whole output on the CPU pool (tests/_cpu_pool.py)
+and otherwise on the pieces named in each test.
 """
 
 import numpy as np
@@ -18,6 +22,8 @@ from oracle.adamw import BF16
 from adamw_optimizer_stochastic_amd import ops
 from adamw_optimizer_stochastic_amd import workloads as wl
 from _gpu_util import gpu, require_gpu, announce, to_host, assert_bits_equal
+import _cpu_pool
+import _oracle_tasks
 
 pytestmark = gpu
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
@@ -32,6 +38,9 @@ def _gpu():
 
 
 def test_convert_2pow30_with_specials():
+    """The conversion workload in the benchmark's launch configuration:
+    2**30 f32 values with 0.1% +-Inf/NaN/FLT_MAX, seed 7, step 0. Every
+    output is compared with the oracle, run in pieces on the CPU pool."""
     n, seed, step = 1 << 30, 7, 0
     announce("convert 2**30: inputs")
     dev = torch.device("cuda", 0)
@@ -46,37 +55,63 @@ def test_convert_2pow30_with_specials():
     announce("convert 2**30: kernel")
     out = ops.cvt_f32_bf16_sr(x, seed, step, 0)
     torch.cuda.synchronize()
-    # Every special position, against the oracle.
+    # Every special position first (names the failing kind of input).
     got_sp = to_host(out[torch.from_numpy(pos).to(dev)])
     want_sp = oracle.sr_bf16(specials, oracle.random16(pos.astype(np.uint64), seed, step))
     assert_bits_equal(got_sp, want_sp, "special positions")
-    # Random windows, against the oracle.
-    for w in range(32):
-        start = int(rng.integers(0, n - (1 << 16)))
-        xs = to_host(x[start:start + (1 << 16)])
-        assert_bits_equal(to_host(out[start:start + (1 << 16)]),
-                          oracle.cvt_f32_bf16_sr(xs, seed, step, start), f"window {start}")
-    # The whole output: each finite value lands on its truncation or the
-    # next value away from zero, NaN follows the quiet rule, and the count
-    # of round-ups matches the dropped fractions within binomial bounds.
-    ups = 0
-    expect = 0.0
-    var = 0.0
-    sl = 1 << 27
-    for s in range(0, n, sl):
-        u = to_host(x[s:s + sl]).view(np.uint32)
-        h = to_host(out[s:s + sl])
-        nan = (u & 0x7FFFFFFF) > 0x7F800000
-        trunc = (u >> 16).astype(np.uint16)
-        assert np.all(h[nan] == (trunc[nan] | 0x40))
-        fin = ~nan
-        d = (h[fin].astype(np.int32) - trunc[fin].astype(np.int32))
-        assert np.all((d == 0) | (d == 1))
-        frac = (u[fin] & 0xFFFF).astype(np.float64) / 65536.0
-        ups += int(d.sum())
-        expect += frac.sum()
-        var += (frac * (1 - frac)).sum()
-    assert abs(ups - expect) < 6 * np.sqrt(var), (ups, expect)
+    # Every output, against the oracle, in pieces of 2**24 on the CPU pool.
+    piece = 1 << 24
+    announce(f"convert 2**30: oracle on {n // piece} pieces, {_cpu_pool.workers()} workers")
+
+    def pieces():
+        for s in range(0, n, piece):
+            yield (to_host(x[s:s + piece]), to_host(out[s:s + piece]), s, seed, step)
+
+    with _cpu_pool.pool() as pool:
+        bad = [d for d in pool.imap_unordered(_oracle_tasks.convert_piece, pieces()) if d]
+    assert not bad, bad[:4]
+
+
+def test_f32_workload_full_size_100_steps():
+    """The f32 workload at its full size: 16,777,216 f32 params ~N(0, 0.02),
+    f32 grads ~N(0, 1e-2) drawn afresh each step, m = v = 0, lr 1e-3, wd
+    0.01, 100 steps, one size-class launch per step (16,384 slots). The
+    state after step 1 and after step 100 must equal the oracle's bit for
+    bit; the oracle runs the 100 steps in 16 pieces on the CPU pool."""
+    n, steps = 1 << 24, 100
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0)
+    dev = torch.device("cuda", 0)
+    announce("f32 16M x 100: inputs")
+    gen = wl.device_generator(dev, wl.CFG_F32, 0)
+    p = wl.device_normal(n, 0.02, gen, dev, torch.float32)
+    p0 = to_host(p)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    grads = np.empty((steps, n), np.float32)
+    ws = ops.make_workspace([n], dev)
+    for t in range(1, steps + 1):
+        g = wl.device_normal(n, 1e-2, gen, dev, torch.float32)
+        grads[t - 1] = to_host(g)
+        ops.adamw_step([p], [g], [m], [v], [0], step=t, workspace=ws, **hp)
+        if t == 1:
+            first = (to_host(p), to_host(m), to_host(v))
+        if t % 25 == 0:
+            announce("f32 16M x 100: step", t)
+    torch.cuda.synchronize()
+    last = (to_host(p), to_host(m), to_host(v))
+    piece = n // 16
+    announce(f"f32 16M x 100: oracle on 16 pieces, {_cpu_pool.workers()} workers")
+
+    def pieces():
+        for s in range(0, n, piece):
+            e = s + piece
+            yield (p0[s:e], np.ascontiguousarray(grads[:, s:e]), [a[s:e] for a in first],
+                   [a[s:e] for a in last], s, hp)
+
+    with _cpu_pool.pool() as pool:
+        bad = [d for r in pool.imap_unordered(_oracle_tasks.f32_steps_piece, pieces())
+               for d in r]
+    assert not bad, bad[:4]
 
 
 def test_268M_whole_equals_8_shards_and_odd_split():
@@ -129,21 +164,38 @@ def test_268M_whole_equals_8_shards_and_odd_split():
 
 def test_llama3_8b_list_two_steps_sampled():
     """The benchmark's call: all 291 tensors in one multi-tensor call, two
-    steps. The oracle runs both steps on windows at the start, middle and
-    end of every tensor and on every RMSNorm weight in full."""
+    steps. Against the oracle (both steps):
+      * every tensor of layers 0 and 31 in full, and 16 random windows of
+        2**20 elements in each of embed_tokens and lm_head (each window run
+        by the oracle with its own base_index), on the CPU pool;
+      * windows at the start, middle and end of every other tensor, and
+        every RMSNorm weight in full, in this process."""
     dev = torch.device("cuda", 0)
     announce("llama3-8b: inputs (96 GB)")
     state = wl.llama3_8b_state(dev, seed=0)
     assert len(state) == 291
     assert sum(t["param"].numel() for t in state) == 8030261248
-    win = 1 << 14
-    samples = []
+    rng = wl.host_rng(wl.CFG_LLAMA, 0, 5)
+    win, big_win, piece = 1 << 14, 1 << 20, 1 << 24
+    samples = []       # checked here: (tensor, start, end, p0, g)
+    pool_pieces = []   # checked on the pool: (tensor, start, end, p0, g)
     for t in state:
         n = t["param"].numel()
+        name = t["name"]
+        if name.startswith("layers.0.") or name.startswith("layers.31."):
+            for s0 in range(0, n, piece):
+                e = min(n, s0 + piece)
+                pool_pieces.append((t, s0, e, to_host(t["param"][s0:e]), to_host(t["grad"][s0:e])))
+            continue
+        if name in ("embed_tokens", "lm_head"):
+            for s0 in sorted(int(x) for x in rng.integers(0, n - big_win, size=16)):
+                pool_pieces.append((t, s0, s0 + big_win, to_host(t["param"][s0:s0 + big_win]),
+                                    to_host(t["grad"][s0:s0 + big_win])))
         starts = [0] if n <= 3 * win else [0, n // 2 - win // 2 + 3, n - win]
-        for s in starts:
-            e = min(n, s + (n if n <= 3 * win else win))
-            samples.append((t, s, e, to_host(t["param"][s:e]), to_host(t["grad"][s:e])))
+        for s0 in starts:
+            e = min(n, s0 + (n if n <= 3 * win else win))
+            samples.append((t, s0, e, to_host(t["param"][s0:e]), to_host(t["grad"][s0:e])))
+    assert sum(e - s0 for _, s0, e, _, _ in pool_pieces) == 2 * 218112000 + 32 * big_win
     ws = ops.make_workspace([t["param"].numel() for t in state], dev)
     lists = ([t["param"] for t in state], [t["grad"] for t in state],
              [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
@@ -164,6 +216,19 @@ def test_llama3_8b_list_two_steps_sampled():
         assert_bits_equal(to_host(t["param"][s:e]), p, what + " param")
         assert_bits_equal(to_host(t["exp_avg"][s:e]), m, what + " m")
         assert_bits_equal(to_host(t["exp_avg_sq"][s:e]), v, what + " v")
+    announce(f"llama3-8b: oracle on {len(pool_pieces)} pieces (layers 0 and 31, "
+             f"embed/lm_head windows), {_cpu_pool.workers()} workers")
+    hp = dict(HP, seed=0)
+
+    def tasks():
+        for t, s, e, hp_, hg in pool_pieces:
+            got = (to_host(t["param"][s:e]), to_host(t["exp_avg"][s:e]),
+                   to_host(t["exp_avg_sq"][s:e]))
+            yield (hp_, hg, got, t["base_index"] + s, 2, hp, f"{t['name']}[{s}:{e}]")
+
+    with _cpu_pool.pool() as pool:
+        bad = [d for r in pool.imap_unordered(_oracle_tasks.bf16_steps_piece, tasks()) for d in r]
+    assert not bad, bad[:4]
     del state, lists
 
 
