@@ -101,13 +101,23 @@ static_assert(sizeof(DevTensor) == 56, "metadata layout");
 
 enum : int { kRoundSR = ASR_ROUND_SR, kRoundRN = ASR_ROUND_RN };
 
+// How a lane's run moves: kRunsElem element by element (buffers misaligned
+// against each other); kRunsEdge with vector accesses when the whole run is
+// inside the tensor, else element by element; kRunsWhole with vector
+// accesses and no per-lane checks (the caller knows every run of the slot
+// is whole, so the branch is uniform and the code straight-line).
+enum : int { kRunsElem = 0, kRunsEdge = 1, kRunsWhole = 2 };
+#ifndef ASR_WHOLE_SLOTS
+#define ASR_WHOLE_SLOTS 1
+#endif
+
 // One lane's run of kVec consecutive elements i0 .. i0+kVec-1 of tensor t,
 // of which lo <= e < hi lie inside the tensor (i0 < 0 only for the first run
 // of a shifted tensor). VEC: the run starts on a vector-aligned address of
 // all four buffers, so a whole run moves with vector accesses (128-bit for
 // f32; 64- or 128-bit for bf16); a cut run, or a tensor without such a
 // shift, moves element by element.
-template <class PT, class GT, int ROUND, int PHASE, bool VEC>
+template <class PT, class GT, int ROUND, int PHASE, int RUNS>
 __device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int lo, int hi,
                                            const Coeffs& c, uint32_t seed, uint32_t step) {
   using PS = typename PT::storage;
@@ -116,7 +126,7 @@ __device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int lo
   const GS* __restrict__ grad = static_cast<const GS*>(t.grad);
   float* __restrict__ m = t.m;
   float* __restrict__ v = t.v;
-  const bool full = VEC && lo == 0 && hi == kVec;
+  const bool full = RUNS == kRunsWhole || (RUNS == kRunsEdge && lo == 0 && hi == kVec);
   float p[kVec], g[kVec], mm[kVec], vv[kVec];
   if (full) {
     load_vec<kNonTemporal, kVec>(param + i0, p);
@@ -160,34 +170,40 @@ __device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int lo
 
 // The phase of a run's first position within its Philox call, (base_index
 // + i0) & 3, is the same for every run of a tensor: (base_index - shift) & 3.
-template <class PT, class GT, int ROUND, bool VEC>
+template <class PT, class GT, int ROUND, int RUNS>
 __device__ __forceinline__ void adamw_run_phase(const DevTensor& t, int64_t i0, int lo, int hi,
                                                  const Coeffs& c, uint32_t seed, uint32_t step) {
   if constexpr (std::is_same_v<PT, BF16> && ROUND == kRoundSR) {
     switch (static_cast<int>((t.base_index - t.shift) & 3u)) {
-      case 0: adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, lo, hi, c, seed, step); break;
-      case 1: adamw_run<PT, GT, ROUND, 1, VEC>(t, i0, lo, hi, c, seed, step); break;
-      case 2: adamw_run<PT, GT, ROUND, 2, VEC>(t, i0, lo, hi, c, seed, step); break;
-      default: adamw_run<PT, GT, ROUND, 3, VEC>(t, i0, lo, hi, c, seed, step); break;
+      case 0: adamw_run<PT, GT, ROUND, 0, RUNS>(t, i0, lo, hi, c, seed, step); break;
+      case 1: adamw_run<PT, GT, ROUND, 1, RUNS>(t, i0, lo, hi, c, seed, step); break;
+      case 2: adamw_run<PT, GT, ROUND, 2, RUNS>(t, i0, lo, hi, c, seed, step); break;
+      default: adamw_run<PT, GT, ROUND, 3, RUNS>(t, i0, lo, hi, c, seed, step); break;
     }
   } else {
-    adamw_run<PT, GT, ROUND, 0, VEC>(t, i0, lo, hi, c, seed, step);
+    adamw_run<PT, GT, ROUND, 0, RUNS>(t, i0, lo, hi, c, seed, step);
   }
 }
 
 // Slot `local` (kSlot elements) of tensor t: one kVec-element run per lane.
-// Lanes past the end of a short last slot get an empty range and touch
-// nothing (no early exit, so the whole descriptor is fetched in one round).
+// A slot whose runs all lie inside a vector-aligned tensor (every slot but
+// the first and last of a tensor) takes the straight-line vector path; at
+// the ends, lanes past either end get an empty range and touch nothing (no
+// early exit, so the whole descriptor is fetched in one round).
 template <class PT, class GT, int ROUND>
 __device__ __forceinline__ void adamw_slot(const DevTensor& t, uint32_t local, const Coeffs& c,
                                            uint32_t seed, uint32_t step) {
-  const int64_t i0 = static_cast<int64_t>(local) * kSlot +
-                     static_cast<int64_t>(threadIdx.x) * kVec - static_cast<int64_t>(t.shift);
+  const int64_t s0 = static_cast<int64_t>(local) * kSlot - static_cast<int64_t>(t.shift);
+  const int64_t i0 = s0 + static_cast<int64_t>(threadIdx.x) * kVec;
+  if (ASR_WHOLE_SLOTS && t.vec_ok && s0 >= 0 && s0 + kSlot <= t.numel) {
+    adamw_run_phase<PT, GT, ROUND, kRunsWhole>(t, i0, 0, kVec, c, seed, step);
+    return;
+  }
   const int64_t left = t.numel - i0;
   const int hi = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
   const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
-  if (t.vec_ok) adamw_run_phase<PT, GT, ROUND, true>(t, i0, lo, hi, c, seed, step);
-  else adamw_run_phase<PT, GT, ROUND, false>(t, i0, lo, hi, c, seed, step);
+  if (t.vec_ok) adamw_run_phase<PT, GT, ROUND, kRunsEdge>(t, i0, lo, hi, c, seed, step);
+  else adamw_run_phase<PT, GT, ROUND, kRunsElem>(t, i0, lo, hi, c, seed, step);
 }
 
 // The multi-tensor step, one slot per workgroup, no loop: the workgroups in
@@ -434,7 +450,7 @@ stream_write(u32x4* __restrict__ dst, uint64_t n16, uint64_t slot0, uint32_t val
 // It measures what HBM gives this access pattern (four streams read, three
 // written) under the step's launch structure; the benchmark reports it
 // beside the step.
-template <class PT, class GT, bool VEC>
+template <class PT, class GT, int RUNS>
 __device__ __forceinline__ void probe_run(const DevTensor& t, int64_t i0, int lo, int hi) {
   using PS = typename PT::storage;
   using GS = typename GT::storage;
@@ -442,7 +458,7 @@ __device__ __forceinline__ void probe_run(const DevTensor& t, int64_t i0, int lo
   const GS* __restrict__ grad = static_cast<const GS*>(t.grad);
   float* __restrict__ m = t.m;
   float* __restrict__ v = t.v;
-  const bool full = VEC && lo == 0 && hi == kVec;
+  const bool full = RUNS == kRunsWhole || (RUNS == kRunsEdge && lo == 0 && hi == kVec);
   float p[kVec], g[kVec], mm[kVec], vv[kVec];
   if (full) {
     load_vec<kNonTemporal, kVec>(param + i0, p);
@@ -478,13 +494,17 @@ __device__ __forceinline__ void probe_run(const DevTensor& t, int64_t i0, int lo
 
 template <class PT, class GT>
 __device__ __forceinline__ void probe_slot(const DevTensor& t, uint32_t local) {
-  const int64_t i0 = static_cast<int64_t>(local) * kSlot +
-                     static_cast<int64_t>(threadIdx.x) * kVec - static_cast<int64_t>(t.shift);
+  const int64_t s0 = static_cast<int64_t>(local) * kSlot - static_cast<int64_t>(t.shift);
+  const int64_t i0 = s0 + static_cast<int64_t>(threadIdx.x) * kVec;
+  if (ASR_WHOLE_SLOTS && t.vec_ok && s0 >= 0 && s0 + kSlot <= t.numel) {
+    probe_run<PT, GT, kRunsWhole>(t, i0, 0, kVec);
+    return;
+  }
   const int64_t left = t.numel - i0;
   const int hi = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
   const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
-  if (t.vec_ok) probe_run<PT, GT, true>(t, i0, lo, hi);
-  else probe_run<PT, GT, false>(t, i0, lo, hi);
+  if (t.vec_ok) probe_run<PT, GT, kRunsEdge>(t, i0, lo, hi);
+  else probe_run<PT, GT, kRunsElem>(t, i0, lo, hi);
 }
 
 // Launched exactly like adamw_sr_class / adamw_sr_slots (same arguments;
