@@ -17,7 +17,7 @@ ASR_OK, ASR_EINVAL, ASR_EDTYPE, ASR_EALIGN, ASR_EWORKSPACE, ASR_EHIP = range(6)
 ASR_F32, ASR_BF16 = 0, 1
 ASR_ROUND_SR, ASR_ROUND_RN = 0, 1
 ASR_PROBE_READ, ASR_PROBE_WRITE, ASR_PROBE_COPY = 0, 1, 2
-ABI_VERSION = 106
+ABI_VERSION = 107
 
 STATUS_NAMES = {ASR_OK: "ASR_OK", ASR_EINVAL: "ASR_EINVAL", ASR_EDTYPE: "ASR_EDTYPE",
                 ASR_EALIGN: "ASR_EALIGN", ASR_EWORKSPACE: "ASR_EWORKSPACE",
@@ -53,6 +53,8 @@ _SIGNATURES = {
     "asr_adamw_step": (_c.c_int, [_c.POINTER(AsrTensor), _c.c_int32] + [_c.c_double] * 5 +
                        [_c.c_int64, _c.c_uint32, _c.c_int32, _c.c_void_p, _c.c_size_t,
                         _c.c_void_p]),
+    "asr_adamw_step_noalloc": (_c.c_int, [_c.POINTER(AsrTensor), _c.c_int32] + [_c.c_double] * 5 +
+                               [_c.c_int64, _c.c_uint32, _c.c_int32, _c.c_void_p]),
     "asr_philox_4x32_fill": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_uint64, _c.c_uint64,
                                         _c.c_uint32, _c.c_uint32, _c.c_void_p]),
     "asr_cvt_f32_bf16_sr": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_uint32,
@@ -148,6 +150,15 @@ def asr_adamw_step(tensors, lr, beta1, beta2, eps, weight_decay, step, seed, rou
     _check(lib().asr_adamw_step(arr if n else None, n, lr, beta1, beta2, eps, weight_decay,
                                 step, seed, rounding, workspace, workspace_bytes, stream),
            "asr_adamw_step")
+
+
+def asr_adamw_step_noalloc(tensors, lr, beta1, beta2, eps, weight_decay, step, seed, rounding,
+                           stream):
+    """asr_adamw_step on the library's static scratch (no workspace)."""
+    arr, n = _tensor_array(tensors)
+    _check(lib().asr_adamw_step_noalloc(arr if n else None, n, lr, beta1, beta2, eps,
+                                        weight_decay, step, seed, rounding, stream),
+           "asr_adamw_step_noalloc")
 
 
 def asr_philox_4x32_fill(out, n_counters, counter_base, counter_upper, seed, step, stream):

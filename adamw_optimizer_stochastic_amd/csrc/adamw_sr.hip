@@ -33,6 +33,7 @@
 #include <map>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <utility>
@@ -113,10 +114,10 @@ enum : int { kRunsElem = 0, kRunsEdge = 1, kRunsWhole = 2 };
 
 // One lane's run of kVec consecutive elements i0 .. i0+kVec-1 of tensor t,
 // of which lo <= e < hi lie inside the tensor (i0 < 0 only for the first run
-// of a shifted tensor). VEC: the run starts on a vector-aligned address of
-// all four buffers, so a whole run moves with vector accesses (128-bit for
-// f32; 64- or 128-bit for bf16); a cut run, or a tensor without such a
-// shift, moves element by element.
+// of a shifted tensor). Whole runs of a tensor with vec_ok start on a
+// vector-aligned address of all four buffers and move with vector accesses
+// (128-bit for f32; 64- or 128-bit for bf16); cut runs, and every run of a
+// tensor without vec_ok, move element by element (RUNS, above).
 template <class PT, class GT, int ROUND, int PHASE, int RUNS>
 __device__ __forceinline__ void adamw_run(const DevTensor& t, int64_t i0, int lo, int hi,
                                            const Coeffs& c, uint32_t seed, uint32_t step) {
@@ -288,6 +289,11 @@ __global__ void __launch_bounds__(kBlock)
 upload_words(UploadBlock src, uint32_t* __restrict__ dst, uint32_t n_words) {
   for (uint32_t i = threadIdx.x; i < n_words; i += kBlock) dst[i] = src.w[i];
 }
+
+// Device workspace of the allocation-free step (see asr_adamw_step_noalloc):
+// 4 MiB, one copy per GPU.
+constexpr size_t kScratchBytes = size_t{4} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 // ---------------------------------------------------------- Philox fill
 __global__ void __launch_bounds__(kBlock)
@@ -965,6 +971,37 @@ int enqueue_plan(const StepPlan& plan, uint8_t* ws, bool probe, int rounding,
   return ok();
 }
 
+// ----------------------------------------------- allocation-free variant
+// The workspace of asr_adamw_step_noalloc: a fixed device array, one copy
+// per GPU, held until the process ends. Host code never passes `scratch`
+// itself to a kernel (on the host that name is a stand-in, not a device
+// address): it uses the address hipGetSymbolAddress returns for the
+// current device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device, looked up on the first call
+// on that device (with it current) and kept.
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ASR_EINVAL, "device index beyond the " + std::to_string(kMaxDevices) +
+                                " devices the scratch table holds");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(asr::scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(ASR_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ASR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1004,6 +1041,27 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors, double lr, doub
   if (int s = check_workspace(plan, workspace, workspace_bytes)) return s;
   const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
   return enqueue_plan(plan, static_cast<uint8_t*>(workspace), false, rounding, c, seed,
+                      static_cast<uint32_t>(step), static_cast<hipStream_t>(stream_ptr));
+}
+
+int asr_adamw_step_noalloc(const asr_tensor* tensors, int32_t n_tensors, double lr,
+                           double beta1, double beta2, double eps, double weight_decay,
+                           int64_t step, uint32_t seed, int32_t rounding, void* stream_ptr) {
+  if (int s = check_hparams(lr, beta1, beta2, eps, weight_decay, step)) return s;
+  if (rounding != ASR_ROUND_SR && rounding != ASR_ROUND_RN)
+    return fail(ASR_EINVAL, "rounding must be ASR_ROUND_SR or ASR_ROUND_RN");
+  StepPlan plan;
+  if (int s = make_plan(tensors, n_tensors, &plan)) return s;
+  if (plan.launches.empty()) return ok();
+  if (plan.used_bytes > asr::kScratchBytes)
+    return fail(ASR_EWORKSPACE, "this list needs " + std::to_string(plan.used_bytes) +
+                                    " bytes of scratch; the static scratch holds " +
+                                    std::to_string(asr::kScratchBytes) +
+                                    " (use asr_adamw_step with a workspace)");
+  void* ws = nullptr;
+  if (int s = current_scratch(&ws)) return s;
+  const asr::Coeffs c = make_coeffs(lr, beta1, beta2, eps, weight_decay, step);
+  return enqueue_plan(plan, static_cast<uint8_t*>(ws), false, rounding, c, seed,
                       static_cast<uint32_t>(step), static_cast<hipStream_t>(stream_ptr));
 }
 

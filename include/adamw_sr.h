@@ -140,6 +140,30 @@ int asr_adamw_step(const asr_tensor* tensors, int32_t n_tensors,
                    void* stream);
 
 /*
+ * asr_adamw_step without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine): its
+ * kernels use a static device array of 4 MiB ("scratch", one copy per GPU,
+ * held until the process ends) in place of the workspace, found on the
+ * first call on each device with that device current. Results are those
+ * of asr_adamw_step bit for bit (the same kernels).
+ * Limit: the list's metadata (60 bytes per tensor plus a few hundred) plus
+ * a 4-byte slot-table entry per 1,024 elements of the tensors that are not
+ * in a size class must fit in 4 MiB (a Llama-3-8B list needs about 18 KiB);
+ * a larger list is rejected with ASR_EWORKSPACE before anything is
+ * enqueued. Nothing in the scratch needs to start at zero: each call
+ * writes all it reads. All calls on one GPU share its scratch, so calls
+ * that may overlap on one GPU (other streams, other threads, several
+ * replays of graphs in flight at once) race: order them on one stream.
+ * Other arguments and errors as for asr_adamw_step.
+ */
+int asr_adamw_step_noalloc(const asr_tensor* tensors, int32_t n_tensors,
+                           double lr, double beta1, double beta2, double eps,
+                           double weight_decay, int64_t step, uint32_t seed,
+                           int32_t rounding, void* stream);
+
+/*
  * The eight binary32 constants asr_adamw_step uses for these
  * hyperparameters, in this order: decay, b1, omb1, b2, omb2, step_size,
  * inv_bc2_sqrt, eps32 (see asr_adamw_step). Host only; touches no device.
@@ -352,7 +376,7 @@ const char* asr_last_error(void);
 /* ABI version of this header and library (major * 100 + minor). */
 int asr_abi_version(void);
 
-#define ASR_ABI_VERSION 106
+#define ASR_ABI_VERSION 107
 
 #ifdef __cplusplus
 }
