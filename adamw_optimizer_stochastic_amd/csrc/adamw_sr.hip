@@ -44,7 +44,13 @@
 
 namespace asr {
 
-constexpr int kBlock = 256;            // 4 waves of 64 lanes
+constexpr int kBlock = 256;            // threads per workgroup of the helper kernels
+// Threads per workgroup of the streaming kernels (the step, its traffic
+// probe and the copy/read/write probes).
+#ifndef ASR_STEP_BLOCK
+#define ASR_STEP_BLOCK 256
+#endif
+constexpr int kStepBlock = ASR_STEP_BLOCK;
 #ifndef ASR_VEC
 #define ASR_VEC 4
 #endif
@@ -58,7 +64,7 @@ constexpr int64_t kCvtSlot = kBlock * kCvtVec;
 #define ASR_CVT_BLOCKS_PER_CU 6
 #endif
 constexpr int kCvtBlocksPerCU = ASR_CVT_BLOCKS_PER_CU;
-constexpr int64_t kSlot = kBlock * kVec;  // elements per workgroup of the step kernel
+constexpr int64_t kSlot = kStepBlock * kVec;  // elements per workgroup of the step kernel
 // Blocks per launch; a larger list is covered by several launches.
 constexpr uint32_t kMaxGrid = 1u << 23;
 // Resident workgroups per CU for the step kernel. The path is bound by HBM
@@ -241,7 +247,7 @@ __device__ __forceinline__ uint32_t slot_of_block(uint32_t b, uint32_t grid) {
 }
 
 template <class PT, class GT, int ROUND>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 adamw_sr_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_tensor, uint32_t magic,
                uint32_t slot0, Coeffs c, uint32_t seed, uint32_t step) {
   const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
@@ -254,7 +260,7 @@ adamw_sr_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_tensor,
 // Table form, for tensors of any sizes: slot_tensor[s] names the tensor of
 // slot s (filled on the device from the tensors' first slots).
 template <class PT, class GT, int ROUND>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 adamw_sr_slots(const DevTensor* __restrict__ tensors, const uint32_t* __restrict__ slot_tensor,
                uint32_t slot0, Coeffs c, uint32_t seed, uint32_t step) {
   const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
@@ -400,24 +406,24 @@ convert_f32_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64
 }
 
 // ------------------------------------------------- measurement: a copy
-// A plain copy built like the step: one slot of kBlock lanes x 4 x 16 bytes
+// A plain copy built like the step: one slot of kStepBlock lanes x 4 x 16 bytes
 // per workgroup, no loop, 128-bit loads and stores, the same XCD windows and
 // residency cap. It measures what this launch structure gets from HBM for
 // a 1:1 read/write stream, the reference the step's bandwidth is also
 // quoted against.
 constexpr int kCopyVec = 4;  // 16-byte units per lane, one wave-wide 1 KiB access each
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16,
             uint64_t slot0) {
-  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kBlock * kCopyVec) +
+  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
                         threadIdx.x;
   u32x4 x[kCopyVec];
 #pragma unroll
   for (int k = 0; k < kCopyVec; ++k)
-    if (base + k * kBlock < n16) x[k] = src[base + k * kBlock];
+    if (base + k * kStepBlock < n16) x[k] = src[base + k * kStepBlock];
 #pragma unroll
   for (int k = 0; k < kCopyVec; ++k)
-    if (base + k * kBlock < n16) dst[base + k * kBlock] = x[k];
+    if (base + k * kStepBlock < n16) dst[base + k * kStepBlock] = x[k];
 }
 
 // A read-only and a write-only stream in the copy's form (one 16 KiB slot
@@ -425,28 +431,28 @@ stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16
 // XOR-ing them and storing the result to sink[0] only if it equals a value
 // that a buffer of equal 16-byte words (the benchmark fills it so) cannot
 // give, so it moves no bytes to memory.
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 stream_read(const u32x4* __restrict__ src, u32x4* __restrict__ sink, uint64_t n16,
             uint64_t slot0) {
-  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kBlock * kCopyVec) +
+  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
                         threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < kCopyVec; ++k)
-    if (base + k * kBlock < n16) acc ^= src[base + k * kBlock];
+    if (base + k * kStepBlock < n16) acc ^= src[base + k * kStepBlock];
   if (acc.x == 0x9E3779B9u && acc.y == 0xBB67AE85u && acc.z == 0xD2511F53u &&
       acc.w == 0xCD9E8D57u)
     sink[0] = acc;
 }
 
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 stream_write(u32x4* __restrict__ dst, uint64_t n16, uint64_t slot0, uint32_t value) {
-  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kBlock * kCopyVec) +
+  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
                         threadIdx.x;
   const u32x4 x = {value, value, value, value};
 #pragma unroll
   for (int k = 0; k < kCopyVec; ++k)
-    if (base + k * kBlock < n16) dst[base + k * kBlock] = x;
+    if (base + k * kStepBlock < n16) dst[base + k * kStepBlock] = x;
 }
 
 // The step's memory traffic with its arithmetic taken out: the same runs,
@@ -516,7 +522,7 @@ __device__ __forceinline__ void probe_slot(const DevTensor& t, uint32_t local) {
 // Launched exactly like adamw_sr_class / adamw_sr_slots (same arguments;
 // the coefficients, seed and step are unused).
 template <class PT, class GT>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 stream_probe_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_tensor,
                    uint32_t magic, uint32_t slot0, Coeffs, uint32_t, uint32_t) {
   const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
@@ -527,7 +533,7 @@ stream_probe_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_ten
 }
 
 template <class PT, class GT>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kStepBlock)
 stream_probe_slots(const DevTensor* __restrict__ tensors, const uint32_t* __restrict__ slot_tensor,
                    uint32_t slot0, Coeffs, uint32_t, uint32_t) {
   const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
@@ -590,15 +596,15 @@ using asr_host::ok;
 // Launches `kernel` with one block size for all kernels of the library;
 // the arguments are converted to the kernel's parameter types first.
 template <typename... KArgs, typename... Args>
-hipError_t launch_lds(void (*kernel)(KArgs...), uint32_t grid, uint32_t lds_bytes,
+hipError_t launch_lds(void (*kernel)(KArgs...), uint32_t grid, uint32_t block, uint32_t lds_bytes,
                       hipStream_t stream, Args&&... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
   std::tuple<KArgs...> vals(std::forward<Args>(args)...);
   return std::apply(
       [&](auto&... v) {
         void* argv[] = {static_cast<void*>(&v)...};
-        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid),
-                               dim3(asr::kBlock), argv, lds_bytes, stream);
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block),
+                               argv, lds_bytes, stream);
       },
       vals);
 }
@@ -606,7 +612,7 @@ hipError_t launch_lds(void (*kernel)(KArgs...), uint32_t grid, uint32_t lds_byte
 template <typename... KArgs, typename... Args>
 hipError_t launch(void (*kernel)(KArgs...), uint32_t grid, hipStream_t stream,
                   Args&&... args) {
-  return launch_lds(kernel, grid, 0, stream, std::forward<Args>(args)...);
+  return launch_lds(kernel, grid, asr::kBlock, 0, stream, std::forward<Args>(args)...);
 }
 
 bool aligned(const void* p, uintptr_t a) {
@@ -825,7 +831,8 @@ hipError_t run_launch(const Launch& l, uint8_t* ws, bool probe, int rounding,
     const uint32_t magic = 0xFFFFFFFFu / l.slots_per_tensor;
     for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
       const uint32_t grid = std::min(n_slots - slot0, asr::kMaxGrid);
-      e = launch_lds(k, grid, lds, stream, d_tensors, l.slots_per_tensor, magic, slot0, c, seed,
+      e = launch_lds(k, grid, asr::kStepBlock, lds, stream, d_tensors, l.slots_per_tensor, magic,
+                     slot0, c, seed,
                      step);
       if (e != hipSuccess) return e;
     }
@@ -842,7 +849,8 @@ hipError_t run_launch(const Launch& l, uint8_t* ws, bool probe, int rounding,
   if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
   for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
     const uint32_t grid = std::min(n_slots - slot0, asr::kMaxGrid);
-    e = launch_lds(k, grid, lds, stream, d_tensors, static_cast<const uint32_t*>(d_table), slot0,
+    e = launch_lds(k, grid, asr::kStepBlock, lds, stream, d_tensors,
+                   static_cast<const uint32_t*>(d_table), slot0,
                    c, seed, step);
     if (e != hipSuccess) return e;
   }
@@ -1130,7 +1138,8 @@ static int convert(int rounding, const float* in, uint16_t* out, int64_t n, uint
   }
   for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
-    hipError_t e = launch_lds(k, grid, lds, stream, in, out, n, slot0, base_index, seed, step,
+    hipError_t e = launch_lds(k, grid, asr::kBlock, lds, stream, in, out, n, slot0, base_index,
+                              seed, step,
                               vec_ok, shift);
     if (e != hipSuccess) return hip_fail(e, "convert launch");
   }
@@ -1153,7 +1162,7 @@ int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream_ptr)
   if (bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
     return fail(ASR_EALIGN, "buffers and size must be multiples of 16 bytes");
   const uint64_t n16 = static_cast<uint64_t>(bytes) / 16;
-  const uint64_t per_slot = static_cast<uint64_t>(asr::kBlock) * asr::kCopyVec;
+  const uint64_t per_slot = static_cast<uint64_t>(asr::kStepBlock) * asr::kCopyVec;
   const uint64_t n_slots = (n16 + per_slot - 1) / per_slot;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   uint32_t lds = 0;
@@ -1161,7 +1170,8 @@ int asr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream_ptr)
   if (e != hipSuccess) return hip_fail(e, "copy attribute");
   for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
-    e = launch_lds(asr::stream_copy, grid, lds, stream, static_cast<const asr::u32x4*>(src),
+    e = launch_lds(asr::stream_copy, grid, asr::kStepBlock, lds, stream,
+                   static_cast<const asr::u32x4*>(src),
                    static_cast<asr::u32x4*>(dst), n16, slot0);
     if (e != hipSuccess) return hip_fail(e, "copy launch");
   }
@@ -1179,7 +1189,7 @@ int asr_hbm_probe(int32_t kind, void* dst, const void* src, int64_t bytes, void*
   if (bytes % 16 != 0 || !aligned(buf, 16) || !aligned(dst, 16))
     return fail(ASR_EALIGN, "buffers and size must be multiples of 16 bytes");
   const uint64_t n16 = static_cast<uint64_t>(bytes) / 16;
-  const uint64_t per_slot = static_cast<uint64_t>(asr::kBlock) * asr::kCopyVec;
+  const uint64_t per_slot = static_cast<uint64_t>(asr::kStepBlock) * asr::kCopyVec;
   const uint64_t n_slots = (n16 + per_slot - 1) / per_slot;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const void* k = kind == ASR_PROBE_READ ? reinterpret_cast<const void*>(asr::stream_read)
@@ -1190,10 +1200,12 @@ int asr_hbm_probe(int32_t kind, void* dst, const void* src, int64_t bytes, void*
   for (uint64_t slot0 = 0; slot0 < n_slots; slot0 += asr::kMaxGrid) {
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>(n_slots - slot0, asr::kMaxGrid));
     if (kind == ASR_PROBE_READ)
-      e = launch_lds(asr::stream_read, grid, lds, stream, static_cast<const asr::u32x4*>(src),
+      e = launch_lds(asr::stream_read, grid, asr::kStepBlock, lds, stream,
+                     static_cast<const asr::u32x4*>(src),
                      static_cast<asr::u32x4*>(dst), n16, slot0);
     else
-      e = launch_lds(asr::stream_write, grid, lds, stream, static_cast<asr::u32x4*>(dst), n16,
+      e = launch_lds(asr::stream_write, grid, asr::kStepBlock, lds, stream,
+                     static_cast<asr::u32x4*>(dst), n16,
                      slot0, 0x3F803F80u);
     if (e != hipSuccess) return hip_fail(e, "probe launch");
   }

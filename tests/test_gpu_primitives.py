@@ -133,20 +133,49 @@ def test_cvt_sr_statistics_on_device():
 
 
 # ------------------------------------------------------ sqrt / division
+def _div_operands(rng, n, kind):
+    """n pairs of f32 patterns: "random" (uniform over all patterns, so every
+    exponent, Inf and NaN), "subnormal_a" / "subnormal_b" (that operand
+    subnormal or zero), "edge" (exponents chosen so the quotient lands near
+    the subnormal range or near overflow)."""
+    a = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    b = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    man, sign = np.uint32(0x807FFFFF), np.uint32(0x80000000)
+    if kind == "subnormal_a":
+        a &= man
+    elif kind == "subnormal_b":
+        b &= man
+    elif kind == "edge":
+        ea = rng.integers(1, 255, size=n, dtype=np.int64)
+        # quotient exponent ea - eb + 127 near 0 (subnormal results) or near 254
+        target = np.where(rng.integers(0, 2, size=n) == 0, rng.integers(-24, 3, size=n),
+                          rng.integers(250, 256, size=n))
+        eb = np.clip(ea - target + 127, 1, 254)
+        a = (a & man) | (ea.astype(np.uint32) << np.uint32(23))
+        b = (b & man) | (eb.astype(np.uint32) << np.uint32(23))
+    return a.view(np.float32), b.view(np.float32)
+
+
 def test_sqrt_div_random_patterns_bit_exact():
-    announce("sqrt/div random patterns")
+    """The kernel's division on 2**28 pairs (16 slices: uniform patterns,
+    subnormal dividends, subnormal divisors, quotients near underflow and
+    overflow) and its sqrt on the dividends, against numpy's correctly
+    rounded float32 operations, bit for bit (NaN-ness only for NaN)."""
     rng = np.random.default_rng(42)
     n = 1 << 24
-    a = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32).view(np.float32)
-    b = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32).view(np.float32)
-    # Also plain positive values of every binade, as the AdamW kernel sees them.
-    a[: n // 4] = np.abs(a[: n // 4])
-    s, d = ops.f32_sqrt_div(f32_tensor(a), f32_tensor(b))
-    with np.errstate(all="ignore"):
-        want_s = np.sqrt(a)
-        want_d = np.divide(a, b)
-    assert_f32_equal_or_both_nan(to_host(s), want_s, "sqrt")
-    assert_f32_equal_or_both_nan(to_host(d), want_d, "div")
+    kinds = ["random"] * 4 + ["subnormal_a"] * 4 + ["subnormal_b"] * 4 + ["edge"] * 4
+    for k, kind in enumerate(kinds):
+        announce("sqrt/div slice", k, kind)
+        a, b = _div_operands(rng, n, kind)
+        if kind == "random":
+            # also plain positive values of every binade, as the AdamW kernel sees them
+            a[: n // 4] = np.abs(a[: n // 4])
+        s, d = ops.f32_sqrt_div(f32_tensor(a), f32_tensor(b))
+        with np.errstate(all="ignore"):
+            want_s = np.sqrt(a)
+            want_d = np.divide(a, b)
+        assert_f32_equal_or_both_nan(to_host(s), want_s, f"sqrt ({kind})")
+        assert_f32_equal_or_both_nan(to_host(d), want_d, f"div ({kind})")
 
 
 def test_sqrt_exhaustive_nonnegative():

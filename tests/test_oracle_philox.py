@@ -96,8 +96,10 @@ def test_matches_triton_interpreter(tmp_path):
 
 
 def test_scalar_equals_vectorized():
+    """The pure-Python scalar form against the numpy form on 2**20 random
+    (counter, key) pairs."""
     rng = np.random.default_rng(7)
-    n = 1 << 14
+    n = 1 << 20
     ctr = rng.integers(0, 1 << 32, size=(4, n), dtype=np.uint64)
     key = rng.integers(0, 1 << 32, size=(2, n), dtype=np.uint64)
     vec = np.stack(oracle.philox4x32_10(*ctr, *key), -1)
