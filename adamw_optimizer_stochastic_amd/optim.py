@@ -11,6 +11,16 @@ when the parameter is added (later groups are appended after it).
 
 Unsupported AdamW options raise NotImplementedError rather than silently
 computing something else.
+
+Moment states live in flat buffers: the f32 exp_avg of every parameter that
+gets its state in one step is a view into one contiguous buffer per device,
+and so is exp_avg_sq, each view starting on a 256-byte boundary (the layout
+of flat-buffer optimizers and ZeRO partitions), allocated once the
+parameters and gradients exist. On MI355X the step over a Llama-3-8B-shaped
+list ran at 6.02-6.10 TB/s with states allocated that way (flat about 1%
+ahead of one allocation per state), and at 5.61-5.62 TB/s when each
+tensor's states were allocated between the parameters, gradients and their
+temporaries, tensor by tensor.
 """
 
 import torch
@@ -78,6 +88,35 @@ class AdamWSR(torch.optim.Optimizer):
         """Global position of element 0 of parameter p."""
         return self._base_index[p]
 
+    @staticmethod
+    def _flat_states(params):
+        """Zero f32 exp_avg / exp_avg_sq views for `params` (one device), in
+        two flat buffers, each view 256-byte aligned."""
+        align = 64
+        offs, total = [], 0
+        for p in params:
+            offs.append(total)
+            total += (p.numel() + align - 1) // align * align
+        dev = params[0].device
+        bufs = (torch.zeros(max(total, 1), dtype=torch.float32, device=dev),
+                torch.zeros(max(total, 1), dtype=torch.float32, device=dev))
+        return [(bufs[0][o:o + p.numel()].view(p.shape), bufs[1][o:o + p.numel()].view(p.shape))
+                for o, p in zip(offs, params)]
+
+    def _init_states(self, params):
+        """Creates the state of every parameter in `params` that has none:
+        step 0 and zero moments in flat buffers per device."""
+        by_dev = {}
+        for p in params:
+            if len(self.state[p]) == 0:
+                by_dev.setdefault(p.device, []).append(p)
+        for ps in by_dev.values():
+            for p, (m, v) in zip(ps, self._flat_states(ps)):
+                # int64, not torch's float32: a float32 count stops at 2**24,
+                # and from there every step would reuse one key (seed, step)
+                self.state[p] = {"step": torch.tensor(0, dtype=torch.int64), "exp_avg": m,
+                                 "exp_avg_sq": v}
+
     def _workspace(self, device, numels):
         """A cached workspace for this device and its current stream. The step
         kernels read their metadata from the workspace asynchronously, so a
@@ -97,25 +136,20 @@ class AdamWSR(torch.optim.Optimizer):
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
+        live = [p for g in self.param_groups for p in g["params"] if p.grad is not None]
+        for p in live:
+            if p.grad.is_sparse:
+                raise NotImplementedError("AdamWSR does not support sparse gradients")
+            if not p.is_contiguous() or not p.grad.is_contiguous():
+                raise NotImplementedError("AdamWSR needs contiguous params and grads")
+        self._init_states(live)
         for group in self.param_groups:
             beta1, beta2 = group["betas"]
             batches = {}  # (device, step) -> lists
             for p in group["params"]:
                 if p.grad is None:
                     continue
-                if p.grad.is_sparse:
-                    raise NotImplementedError("AdamWSR does not support sparse gradients")
-                if not p.is_contiguous() or not p.grad.is_contiguous():
-                    raise NotImplementedError("AdamWSR needs contiguous params and grads")
                 state = self.state[p]
-                if len(state) == 0:
-                    # int64, not torch's float32: a float32 count stops at 2**24,
-                    # and from there every step would reuse one key (seed, step)
-                    state["step"] = torch.tensor(0, dtype=torch.int64)
-                    state["exp_avg"] = torch.zeros_like(p, dtype=torch.float32,
-                                                        memory_format=torch.contiguous_format)
-                    state["exp_avg_sq"] = torch.zeros_like(p, dtype=torch.float32,
-                                                           memory_format=torch.contiguous_format)
                 state["step"] += 1
                 t = int(state["step"].item())
                 key = (p.device, t)
@@ -147,15 +181,15 @@ class AdamWSR(torch.optim.Optimizer):
         super().load_state_dict(plain)
         saved_ids = [i for g in state_dict["param_groups"] for i in g["params"]]
         params = [p for g in self.param_groups for p in g["params"]]
-        for pid, p in zip(saved_ids, params):
-            st = saved_state.get(pid)
-            if st is None:
-                continue
-            self.state[p] = {
-                "step": torch.tensor(_step_count(st["step"]), dtype=torch.int64),
-                "exp_avg": st["exp_avg"].detach().to(device=p.device, dtype=torch.float32).clone(),
-                "exp_avg_sq": st["exp_avg_sq"].detach().to(device=p.device,
-                                                            dtype=torch.float32).clone(),
-            }
+        loaded = [(p, saved_state[pid]) for pid, p in zip(saved_ids, params)
+                  if saved_state.get(pid) is not None]
+        for p, _ in loaded:
+            self.state[p] = {}
+        self._init_states([p for p, _ in loaded])   # flat buffers, then the saved values
+        for p, st in loaded:
+            state = self.state[p]
+            state["step"].fill_(_step_count(st["step"]))
+            state["exp_avg"].copy_(st["exp_avg"].detach().reshape(p.shape))
+            state["exp_avg_sq"].copy_(st["exp_avg_sq"].detach().reshape(p.shape))
         if extra is not None:
             self.seed = int(extra["seed"])

@@ -17,7 +17,9 @@ Workloads (sizes as used by the tests and the benchmark):
   * shards:  268,435,456 bf16 params ~N(0, 0.02), bf16 grads ~N(0, 1e-3);
   * llama3_8b: the parameter list of a Llama-3-8B-shaped model (291
              tensors, 8,030,261,248 elements), bf16 matrices ~N(0, 0.02),
-             RMSNorm weights 1.0, bf16 grads ~N(0, 1e-3), f32 m = v = 0.
+             RMSNorm weights 1.0, bf16 grads ~N(0, 1e-3), f32 m = v = 0
+             allocated after params and grads, in flat buffers as the
+             optimizer allocates them (or per tensor, on request).
   * llama3_8b rank share: what one of R data-parallel ranks holds when the
              flattened list is split into R equal contiguous ranges (the
              ZeRO-1 layout): the pieces of the tensors inside its range,
@@ -118,9 +120,35 @@ def device_normal(n, std, gen, device, dtype):
     return x if dtype == torch.float32 else x.to(dtype)
 
 
-def llama3_8b_state(device, seed=0, param_std=0.02, grad_std=1e-3, cfg=LLAMA3_8B):
+STATE_ALIGN = 64  # elements of f32: flat-state views start on 256-byte boundaries
+
+
+def zero_states(numels, device, layout="flat"):
+    """f32 zero moment states (exp_avg, exp_avg_sq) for tensors of these
+    sizes, allocated after the parameters and gradients as an optimizer
+    does at its first step. "flat": two buffers, one per moment, each
+    tensor's state a view starting on a 256-byte boundary (the layout
+    AdamWSR allocates); "separate": one allocation per state, per tensor in
+    turn (the layout of zeros_like per parameter)."""
+    if layout == "separate":
+        return [(torch.zeros(n, dtype=torch.float32, device=device),
+                 torch.zeros(n, dtype=torch.float32, device=device)) for n in numels]
+    if layout != "flat":
+        raise ValueError(layout)
+    offs, total = [], 0
+    for n in numels:
+        offs.append(total)
+        total += (n + STATE_ALIGN - 1) // STATE_ALIGN * STATE_ALIGN
+    m = torch.zeros(max(total, 1), dtype=torch.float32, device=device)
+    v = torch.zeros(max(total, 1), dtype=torch.float32, device=device)
+    return [(m[o:o + n], v[o:o + n]) for o, n in zip(offs, numels)]
+
+
+def llama3_8b_state(device, seed=0, param_std=0.02, grad_std=1e-3, cfg=LLAMA3_8B,
+                    states="flat"):
     """Allocates the full list on `device`: list of dicts with name, param,
-    grad, exp_avg, exp_avg_sq, base_index (running total of numel)."""
+    grad, exp_avg, exp_avg_sq, base_index (running total of numel). Params
+    and grads first (the model), then the moment states (see zero_states)."""
     gen = device_generator(device, CFG_LLAMA, seed)
     out, base = [], 0
     for name, shape in llama3_8b_shapes(cfg):
@@ -130,11 +158,10 @@ def llama3_8b_state(device, seed=0, param_std=0.02, grad_std=1e-3, cfg=LLAMA3_8B
         else:
             p = device_normal(n, param_std, gen, device, torch.bfloat16)
         g = device_normal(n, grad_std, gen, device, torch.bfloat16)
-        out.append(dict(name=name, param=p, grad=g,
-                        exp_avg=torch.zeros(n, dtype=torch.float32, device=device),
-                        exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=device),
-                        base_index=base))
+        out.append(dict(name=name, param=p, grad=g, base_index=base))
         base += n
+    for t, (m, v) in zip(out, zero_states([t["param"].numel() for t in out], device, states)):
+        t["exp_avg"], t["exp_avg_sq"] = m, v
     return out
 
 
@@ -158,9 +185,10 @@ def llama3_8b_rank_pieces(rank, ranks, cfg=LLAMA3_8B):
 
 
 def llama3_8b_rank_state(device, rank, ranks, seed=0, param_std=0.02, grad_std=1e-3,
-                         cfg=LLAMA3_8B):
+                         cfg=LLAMA3_8B, states="flat"):
     """Allocates one rank's pieces on `device`: list of dicts with name,
-    offset, param, grad, exp_avg, exp_avg_sq, base_index."""
+    offset, param, grad, exp_avg, exp_avg_sq, base_index (states as in
+    llama3_8b_state)."""
     gen = device_generator(device, CFG_RANK, seed, rank)
     out = []
     for name, shape, off, n, base in llama3_8b_rank_pieces(rank, ranks, cfg):
@@ -169,10 +197,9 @@ def llama3_8b_rank_state(device, rank, ranks, seed=0, param_std=0.02, grad_std=1
         else:
             p = device_normal(n, param_std, gen, device, torch.bfloat16)
         g = device_normal(n, grad_std, gen, device, torch.bfloat16)
-        out.append(dict(name=name, offset=off, param=p, grad=g,
-                        exp_avg=torch.zeros(n, dtype=torch.float32, device=device),
-                        exp_avg_sq=torch.zeros(n, dtype=torch.float32, device=device),
-                        base_index=base))
+        out.append(dict(name=name, offset=off, param=p, grad=g, base_index=base))
+    for t, (m, v) in zip(out, zero_states([t["param"].numel() for t in out], device, states)):
+        t["exp_avg"], t["exp_avg_sq"] = m, v
     return out
 
 

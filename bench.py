@@ -185,10 +185,11 @@ def run_adamw(args, torch, ops, wl):
     torch.cuda.set_device(dev)
     extra = {}
     if args.workload == "llama3_8b":
-        state = wl.llama3_8b_state(dev, seed=0)
+        state = wl.llama3_8b_state(dev, seed=0, states=args.state_layout)
         cfg_name = "llama3_8b_param_list"
     elif args.workload == "llama3_8b_rank":
-        state = wl.llama3_8b_rank_state(dev, args.rank, args.ranks, seed=0)
+        state = wl.llama3_8b_rank_state(dev, args.rank, args.ranks, seed=0,
+                                        states=args.state_layout)
         cfg_name = f"llama3_8b_rank{args.rank}_of_{args.ranks}"
         extra = {"rank": args.rank, "ranks": args.ranks,
                  "first_piece": [state[0]["name"], state[0]["offset"]],
@@ -257,6 +258,8 @@ def run_adamw(args, torch, ops, wl):
         "config": {"workload": cfg_name, "n_tensors": len(state), "params": n_elems,
                    "param_dtype": "bf16", "grad_dtype": "bf16", "state_dtype": "f32",
                    "rounding": "sr", "algorithmic_bytes_per_param": 22,
+                   "state_layout": STATE_LAYOUT_NOTE[args.state_layout]
+                   if args.workload != "shards" else "one tensor",
                    "parallelism": "single GPU", **extra},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -332,6 +335,11 @@ def stream_copy_gbps(torch, dev, stream, nbytes=8 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+STATE_LAYOUT_NOTE = {
+    "flat": "flat: f32 m and v of all tensors in two buffers, allocated after params and "
+            "grads (AdamWSR's layout)",
+    "separate": "separate: one f32 m and one f32 v allocation per tensor, after params and "
+                "grads (zeros_like per parameter)"}
 SHARDS_ODD_CUT = 33554433
 
 
@@ -582,7 +590,7 @@ def run_hbm_probe(args, torch, ops, wl):
     del src, dst
     torch.cuda.empty_cache()
 
-    state = wl.llama3_8b_state(dev, seed=0)
+    state = wl.llama3_8b_state(dev, seed=0, states=args.state_layout)
     n_elems = sum(t["param"].numel() for t in state)
     lists = ([t["param"] for t in state], [t["grad"] for t in state],
              [t["exp_avg"] for t in state], [t["exp_avg_sq"] for t in state],
@@ -613,6 +621,7 @@ def run_hbm_probe(args, torch, ops, wl):
         "warmup": args.warmup, "ms_per_step": pr, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u32", "data": "synthetic",
         "config": {"workload": "hbm_probe_llama3_8b_param_list", "params": n_elems,
+                   "state_layout": STATE_LAYOUT_NOTE[args.state_layout],
                    "algorithmic_bytes_per_param": 22, "simple_stream_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": probe_gbps, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": probe_gbps / HBM_PEAK_GBS, "traffic": None,
@@ -658,6 +667,8 @@ def main():
                     "llama3_8b_rank times")
     ap.add_argument("--ranks", type=int, default=8)
     ap.add_argument("--gemm-shape", default=None, help="M,N,K for --workload gemm")
+    ap.add_argument("--state-layout", default="flat", choices=["flat", "separate"],
+                    help="how the Llama lists' f32 moment states are allocated")
     ap.add_argument("--odd-split", action="store_true", help="--workload shards: time the "
                     "tensor as two pieces cut at an odd element")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -102,3 +102,27 @@ def test_step_count_passes_2pow24(monkeypatch):
     sd["state"][0]["step"] = torch.tensor(5.0)
     opt2.load_state_dict(sd)
     assert int(opt2.state[p2]["step"]) == 5
+
+
+def test_moment_states_are_views_of_flat_buffers():
+    """AdamWSR's f32 moment states of the parameters that get their state
+    together are views into one buffer per moment, 256-byte aligned, zero,
+    in the parameters' shapes; a later parameter gets buffers of its own."""
+    ps = [torch.nn.Parameter(torch.zeros(s, dtype=torch.bfloat16)) for s in ((3, 5), (7,), (64,))]
+    late = torch.nn.Parameter(torch.zeros(9))
+    opt = AdamWSR(ps + [late])
+    opt._init_states(ps)
+    for key in ("exp_avg", "exp_avg_sq"):
+        ts = [opt.state[p][key] for p in ps]
+        assert len({t.untyped_storage().data_ptr() for t in ts}) == 1
+        assert [t.shape for t in ts] == [p.shape for p in ps]
+        assert all(t.dtype == torch.float32 and not t.any() for t in ts)
+        assert all(t.storage_offset() % 64 == 0 for t in ts)
+        assert [t.storage_offset() for t in ts] == [0, 64, 128]
+    assert opt.state[ps[0]]["exp_avg"].untyped_storage().data_ptr() != \
+        opt.state[ps[0]]["exp_avg_sq"].untyped_storage().data_ptr()
+    assert len(opt.state[late]) == 0
+    opt._init_states([late] + ps)          # only the parameter without state gets one
+    assert opt.state[late]["exp_avg"].untyped_storage().data_ptr() != \
+        opt.state[ps[0]]["exp_avg"].untyped_storage().data_ptr()
+    assert int(opt.state[late]["step"]) == 0
