@@ -98,11 +98,14 @@ struct DevTensor {
   // so that every run starts on a vector-aligned address of all four
   // buffers (16 bytes for f32, 2*kVec bytes for bf16); vec_ok says such a
   // shift exists, else (buffers misaligned against each other) every
-  // element moves on its own and shift is 0.
-  uint8_t vec_ok;
-  uint8_t shift;
-  uint16_t reserved;
+  // element moves on its own and shift is 0. Both sit in one 32-bit word
+  // (bit 0: vec_ok, bits 8..15: shift) so that the descriptor is read with
+  // scalar loads only (a sub-word field would be read with a vector load
+  // that every lane then waits for).
+  uint32_t runs;
   uint32_t first_slot;  // index of the tensor's first slot within its group
+  __device__ __host__ bool vec_ok() const { return (runs & 1u) != 0; }
+  __device__ __host__ uint32_t shift() const { return (runs >> 8) & 0xFFu; }
 };
 static_assert(sizeof(DevTensor) == 56, "metadata layout");
 
@@ -181,7 +184,7 @@ template <class PT, class GT, int ROUND, int RUNS>
 __device__ __forceinline__ void adamw_run_phase(const DevTensor& t, int64_t i0, int lo, int hi,
                                                  const Coeffs& c, uint32_t seed, uint32_t step) {
   if constexpr (std::is_same_v<PT, BF16> && ROUND == kRoundSR) {
-    switch (static_cast<int>((t.base_index - t.shift) & 3u)) {
+    switch (static_cast<int>((t.base_index - t.shift()) & 3u)) {
       case 0: adamw_run<PT, GT, ROUND, 0, RUNS>(t, i0, lo, hi, c, seed, step); break;
       case 1: adamw_run<PT, GT, ROUND, 1, RUNS>(t, i0, lo, hi, c, seed, step); break;
       case 2: adamw_run<PT, GT, ROUND, 2, RUNS>(t, i0, lo, hi, c, seed, step); break;
@@ -200,16 +203,16 @@ __device__ __forceinline__ void adamw_run_phase(const DevTensor& t, int64_t i0, 
 template <class PT, class GT, int ROUND>
 __device__ __forceinline__ void adamw_slot(const DevTensor& t, uint32_t local, const Coeffs& c,
                                            uint32_t seed, uint32_t step) {
-  const int64_t s0 = static_cast<int64_t>(local) * kSlot - static_cast<int64_t>(t.shift);
+  const int64_t s0 = static_cast<int64_t>(local) * kSlot - static_cast<int64_t>(t.shift());
   const int64_t i0 = s0 + static_cast<int64_t>(threadIdx.x) * kVec;
-  if (ASR_WHOLE_SLOTS && t.vec_ok && s0 >= 0 && s0 + kSlot <= t.numel) {
+  if (ASR_WHOLE_SLOTS && t.vec_ok() && s0 >= 0 && s0 + kSlot <= t.numel) {
     adamw_run_phase<PT, GT, ROUND, kRunsWhole>(t, i0, 0, kVec, c, seed, step);
     return;
   }
   const int64_t left = t.numel - i0;
   const int hi = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
   const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
-  if (t.vec_ok) adamw_run_phase<PT, GT, ROUND, kRunsEdge>(t, i0, lo, hi, c, seed, step);
+  if (t.vec_ok()) adamw_run_phase<PT, GT, ROUND, kRunsEdge>(t, i0, lo, hi, c, seed, step);
   else adamw_run_phase<PT, GT, ROUND, kRunsElem>(t, i0, lo, hi, c, seed, step);
 }
 
@@ -224,21 +227,27 @@ __device__ __forceinline__ void adamw_slot(const DevTensor& t, uint32_t local, c
 // falls short of the true quotient by at most one (s < 2**32), then
 // corrected; the descriptor table is small and stays in the scalar cache.
 #ifndef ASR_WINDOWS
-#define ASR_WINDOWS 8
+#define ASR_WINDOWS 4
 #endif
 // Workgroup -> slot. MI355X hands workgroups to its 8 XCDs round-robin in
-// dispatch order. With kWindows windows (a multiple of 8), workgroup b takes
-// the next slot of window b % kWindows, a contiguous 1/kWindows of the
-// launch, so each XCD works through its own windows. Several narrow windows
-// instead of one average the DRAM bank/channel conflicts between the seven
-// streams over unrelated sets of physical pages (measured on MI355X: 5.33 to
-// 6.28 TB/s across buffer placements with one window, 5.76 to 5.79 with
-// eight). Any bijection is correct; this only changes the order of work.
+// dispatch order. With kWindows windows, workgroup b takes the next slot of
+// window b % kWindows, a contiguous 1/kWindows of the launch; with 4, XCDs x
+// and x + 4 share window x. Several windows instead of one average the DRAM
+// bank/channel conflicts between the seven streams over unrelated sets of
+// physical pages (5.33 to 6.28 TB/s across buffer placements with one
+// window); measured on the Llama-3-8B list in three processes, alternating
+// builds: 1, 2, 4, 8 and 16 windows gave 5.61-5.76, 5.83-5.98, 5.85-6.12,
+// 5.67-5.97 and 5.38-5.63 TB/s. Any bijection is correct; this only changes
+// the order of work.
 constexpr uint32_t kWindows = ASR_WINDOWS;
+// The plain copy, read and write streams measured best with one window per
+// XCD (8); they keep that.
+constexpr uint32_t kCopyWindows = 8;
+template <uint32_t W = kWindows>
 __device__ __forceinline__ uint32_t slot_of_block(uint32_t b, uint32_t grid) {
-  if constexpr (kWindows > 1) {
-    const uint32_t w = b % kWindows, k = b / kWindows;
-    const uint32_t q = grid / kWindows, r = grid % kWindows;
+  if constexpr (W > 1) {
+    const uint32_t w = b % W, k = b / W;
+    const uint32_t q = grid / W, r = grid % W;
     return w * q + (w < r ? w : r) + k;
   } else {
     (void)grid;
@@ -406,16 +415,17 @@ convert_f32_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64
 }
 
 // ------------------------------------------------- measurement: a copy
-// A plain copy built like the step: one slot of kStepBlock lanes x 4 x 16 bytes
-// per workgroup, no loop, 128-bit loads and stores, the same XCD windows and
-// residency cap. It measures what this launch structure gets from HBM for
-// a 1:1 read/write stream, the reference the step's bandwidth is also
-// quoted against.
+// A plain copy built like the step: one slot of kStepBlock lanes x 4 x 16
+// bytes per workgroup, no loop, 128-bit loads and stores, the step's
+// residency cap, and one address window per XCD (the copy's best; the step
+// itself runs best on 4). It measures what this launch structure gets from
+// HBM for a 1:1 read/write stream, the reference the step's bandwidth is
+// also quoted against.
 constexpr int kCopyVec = 4;  // 16-byte units per lane, one wave-wide 1 KiB access each
 __global__ void __launch_bounds__(kStepBlock)
 stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16,
             uint64_t slot0) {
-  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
+  const uint64_t base = (slot0 + slot_of_block<kCopyWindows>(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
                         threadIdx.x;
   u32x4 x[kCopyVec];
 #pragma unroll
@@ -434,7 +444,7 @@ stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16
 __global__ void __launch_bounds__(kStepBlock)
 stream_read(const u32x4* __restrict__ src, u32x4* __restrict__ sink, uint64_t n16,
             uint64_t slot0) {
-  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
+  const uint64_t base = (slot0 + slot_of_block<kCopyWindows>(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
                         threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -447,7 +457,7 @@ stream_read(const u32x4* __restrict__ src, u32x4* __restrict__ sink, uint64_t n1
 
 __global__ void __launch_bounds__(kStepBlock)
 stream_write(u32x4* __restrict__ dst, uint64_t n16, uint64_t slot0, uint32_t value) {
-  const uint64_t base = (slot0 + slot_of_block(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
+  const uint64_t base = (slot0 + slot_of_block<kCopyWindows>(blockIdx.x, gridDim.x)) * (kStepBlock * kCopyVec) +
                         threadIdx.x;
   const u32x4 x = {value, value, value, value};
 #pragma unroll
@@ -506,16 +516,16 @@ __device__ __forceinline__ void probe_run(const DevTensor& t, int64_t i0, int lo
 
 template <class PT, class GT>
 __device__ __forceinline__ void probe_slot(const DevTensor& t, uint32_t local) {
-  const int64_t s0 = static_cast<int64_t>(local) * kSlot - static_cast<int64_t>(t.shift);
+  const int64_t s0 = static_cast<int64_t>(local) * kSlot - static_cast<int64_t>(t.shift());
   const int64_t i0 = s0 + static_cast<int64_t>(threadIdx.x) * kVec;
-  if (ASR_WHOLE_SLOTS && t.vec_ok && s0 >= 0 && s0 + kSlot <= t.numel) {
+  if (ASR_WHOLE_SLOTS && t.vec_ok() && s0 >= 0 && s0 + kSlot <= t.numel) {
     probe_run<PT, GT, kRunsWhole>(t, i0, 0, kVec);
     return;
   }
   const int64_t left = t.numel - i0;
   const int hi = left <= 0 ? 0 : (left < kVec ? static_cast<int>(left) : kVec);
   const int lo = i0 < 0 ? static_cast<int>(-i0) : 0;
-  if (t.vec_ok) probe_run<PT, GT, kRunsEdge>(t, i0, lo, hi);
+  if (t.vec_ok()) probe_run<PT, GT, kRunsEdge>(t, i0, lo, hi);
   else probe_run<PT, GT, kRunsElem>(t, i0, lo, hi);
 }
 
@@ -667,7 +677,7 @@ uint64_t slots_of(int64_t numel) {
 }
 
 // Slots of a tensor: its runs start `shift` elements before element 0.
-uint64_t tensor_slots(const asr::DevTensor& d) { return slots_of(d.numel + d.shift); }
+uint64_t tensor_slots(const asr::DevTensor& d) { return slots_of(d.numel + d.shift()); }
 
 // The most slots a tensor of this size can take, whatever its shift (the
 // workspace size must not depend on where the buffers are).
@@ -901,9 +911,7 @@ int make_plan(const asr_tensor* tensors, int32_t n_tensors, StepPlan* plan) {
     d.numel = t.numel;
     d.base_index = t.base_index;
     const int shift = vector_shift(t);
-    d.vec_ok = shift >= 0;
-    d.shift = static_cast<uint8_t>(shift >= 0 ? shift : 0);
-    d.reserved = 0;
+    d.runs = shift >= 0 ? 1u | (static_cast<uint32_t>(shift) << 8) : 0u;
     d.first_slot = 0;  // set by the launch plan
     group[g].push_back(d);
     group_slots[g] += tensor_slots(d);

@@ -309,7 +309,7 @@ int asr_dropout(const void* x, void* y, uint8_t* mask, int32_t dtype,
 /*
  * Measurement support: copies `bytes` bytes from src to dst with a kernel
  * built like the AdamW step (one slot of 16 KiB per workgroup, 128-bit loads
- * and stores, the step's XCD windows and residency cap). The benchmark
+ * and stores, the step's residency cap; one address window per XCD). The benchmark
  * quotes the step's bandwidth against this copy's as well as against the
  * HBM peak. src, dst: device, 16-byte aligned, not overlapping; bytes a
  * multiple of 16. Errors: ASR_EINVAL, ASR_EALIGN, ASR_EHIP.
