@@ -363,6 +363,8 @@ def whole_vs_odd_split(torch, ops, state, ws, stream, steps):
     whole = [dict(name="w", base_index=base["base_index"],
                   **{k: base[k].as_strided((n,), (1,)) for k in
                      ("param", "grad", "exp_avg", "exp_avg_sq")})]
+    # one workspace that serves both forms (the two pieces need the larger)
+    ws = ops.make_workspace([p["param"].numel() for p in pieces], pieces[0]["param"].device)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0,
               rounding="sr", workspace=ws)
     forms = {}
@@ -562,34 +564,16 @@ def run_rng(args, torch, ops, wl):
 
 def run_hbm_probe(args, torch, ops, wl):
     """What HBM gives the step's launch structure, without its arithmetic:
-    read-only, write-only and 1:1 copy streams (asr_hbm_probe, 16 GiB each
-    way), then the Llama-3-8B list's 4-read/3-write traffic
-    (asr_adamw_stream_probe) against the step itself, alternated in three
-    blocks so that drift during the run favours neither."""
+    the Llama-3-8B list's 4-read/3-write traffic (asr_adamw_stream_probe)
+    against the step itself, alternated in three blocks so that drift during
+    the run favours neither, with the list allocated first, as in the
+    default benchmark; then read-only, write-only and 1:1 copy streams
+    (asr_hbm_probe, 16 GiB each way) in the memory left."""
     from adamw_optimizer_stochastic_amd import _abi
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
-    nbytes = 16 << 30
-    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    simple = {}
-    for name, kind, moved in (("read", _abi.ASR_PROBE_READ, nbytes),
-                              ("write", _abi.ASR_PROBE_WRITE, nbytes),
-                              ("copy", _abi.ASR_PROBE_COPY, 2 * nbytes)):
-        def fn(kind=kind):
-            _abi.asr_hbm_probe(kind, dst.data_ptr(), src.data_ptr(), nbytes, s)
-        for _ in range(max(2, args.warmup)):
-            fn()
-        ms = _time_launches(torch, stream, fn, args.steps)[1]
-        simple[name] = {"bytes_per_launch": moved, "ms": ms,
-                        "GBps": moved / (ms * 1e-3) / 1e9}
-        print(f"[bench] hbm probe {name}: {simple[name]['GBps']:.0f} GB/s", file=sys.stderr,
-              flush=True)
-    del src, dst
-    torch.cuda.empty_cache()
-
     state = wl.llama3_8b_state(dev, seed=0, states=args.state_layout)
     n_elems = sum(t["param"].numel() for t in state)
     lists = ([t["param"] for t in state], [t["grad"] for t in state],
@@ -614,6 +598,24 @@ def run_hbm_probe(args, torch, ops, wl):
     st, pr = sum(step_ms) / 3, sum(probe_ms) / 3
     step_gbps = bytes_per_launch / (st * 1e-3) / 1e9
     probe_gbps = bytes_per_launch / (pr * 1e-3) / 1e9
+
+    nbytes = 16 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    simple = {}
+    for name, kind, moved in (("read", _abi.ASR_PROBE_READ, nbytes),
+                              ("write", _abi.ASR_PROBE_WRITE, nbytes),
+                              ("copy", _abi.ASR_PROBE_COPY, 2 * nbytes)):
+        def fn(kind=kind):
+            _abi.asr_hbm_probe(kind, dst.data_ptr(), src.data_ptr(), nbytes, s)
+        for _ in range(max(2, args.warmup)):
+            fn()
+        ms = _time_launches(torch, stream, fn, args.steps)[1]
+        simple[name] = {"bytes_per_launch": moved, "ms": ms,
+                        "GBps": moved / (ms * 1e-3) / 1e9}
+        print(f"[bench] hbm probe {name}: {simple[name]['GBps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    del src, dst
     return {
         "metric": "HBM GB/s of the AdamW-SR step's access pattern without its arithmetic "
                   "(4 streams read, 3 written), 1 GPU",
