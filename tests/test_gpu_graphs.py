@@ -94,3 +94,62 @@ def test_graph_replays_match_eager():
         assert_bits_equal(got[5], want[5], f"replay {r} dropout")
     # the replays really advanced the state: replay 3 differs from replay 1
     assert not np.array_equal(ref[0][0][0], ref[2][0][0])
+
+
+def test_graph_noalloc_step_replays_match_eager():
+    """asr_adamw_step_noalloc -- the step for callers that cannot allocate,
+    e.g. under graph capture -- captured once (after one eager call, which
+    finds the device's scratch) and replayed three times with eager work in
+    between: each replay equals the same eager step bit for bit."""
+    from adamw_optimizer_stochastic_amd import _abi
+    dev = torch.device("cuda", 0)
+    announce("graph capture noalloc: inputs")
+    gen = wl.device_generator(dev, wl.CFG_SMALL, 43)
+    sizes = [(1 << 21) + 77, 3000, 65537]
+    p0 = [wl.device_normal(n, 0.02, gen, dev, torch.bfloat16) for n in sizes]
+    grads = [wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16) for n in sizes]
+    bases = [5, 5 + sizes[0], 5 + sizes[0] + sizes[1]]
+
+    def fresh():
+        return dict(p=[t.clone() for t in p0],
+                    m=[torch.zeros(t.numel(), dtype=torch.float32, device=dev) for t in p0],
+                    v=[torch.zeros(t.numel(), dtype=torch.float32, device=dev) for t in p0])
+
+    def step(st, t):
+        descs = [_abi.AsrTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel(),
+                                b, _abi.ASR_BF16, _abi.ASR_BF16)
+                 for p, g, m, v, b in zip(st["p"], grads, st["m"], st["v"], bases)]
+        _abi.asr_adamw_step_noalloc(descs, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"],
+                                    HP["weight_decay"], t, 3, _abi.ASR_ROUND_SR,
+                                    torch.cuda.current_stream(dev).cuda_stream)
+
+    def snapshot(st):
+        return [to_host(x) for key in ("p", "m", "v") for x in st[key]]
+
+    announce("graph capture noalloc: eager reference")
+    eager = fresh()
+    ref = []
+    for _ in range(3):
+        step(eager, 2)
+        torch.cuda.synchronize()
+        ref.append(snapshot(eager))
+    del eager
+    st = fresh()
+    warm = fresh()
+    step(warm, 2)                # the first call on the device looks up the scratch
+    torch.cuda.synchronize()
+    del warm
+    announce("graph capture noalloc: capture")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(st, 2)
+    torch.cuda.synchronize()
+    for r in range(3):
+        announce("graph capture noalloc: replay", r)
+        graph.replay()
+        z = torch.ones(1 << 16, device=dev)
+        assert float(z.sum()) == float(1 << 16)
+        torch.cuda.synchronize()
+        for i, (g_, w_) in enumerate(zip(snapshot(st), ref[r])):
+            assert_bits_equal(g_, w_, f"replay {r} array {i}")
+    assert not np.array_equal(ref[0][0], ref[2][0])
