@@ -266,6 +266,45 @@ adamw_sr_class(const DevTensor* __restrict__ tensors, uint32_t slots_per_tensor,
   adamw_slot<PT, GT, ROUND>(t, slot - ti * slots_per_tensor, c, seed, step);
 }
 
+// Inline form, for lists of at most kInlineTensors tensors per launch: the
+// descriptors travel in the kernel arguments, so a small step needs neither
+// an upload launch nor a slot table. A workgroup finds its tensor as the
+// class form does (equal sizes: a multiply-high division), or else by a
+// binary search of the first slots (at most 6 probes); both are
+// wave-uniform, on scalar loads from the kernel-argument segment.
+#ifndef ASR_INLINE_TENSORS
+#define ASR_INLINE_TENSORS 48
+#endif
+constexpr int kInlineTensors = ASR_INLINE_TENSORS;
+struct InlineTensors {
+  DevTensor t[kInlineTensors > 0 ? kInlineTensors : 1];  // first_slot ascending from 0
+  uint32_t n;
+  uint32_t per, magic;  // size class: slots per tensor and its magic; per = 0: any sizes
+};
+
+__device__ __forceinline__ uint32_t inline_tensor(const InlineTensors& L, uint32_t slot) {
+  if (L.per != 0) {
+    uint32_t ti = __umulhi(slot, L.magic);
+    if (static_cast<uint64_t>(ti + 1) * L.per <= slot) ++ti;
+    return ti;
+  }
+  uint32_t lo = 0, hi = L.n - 1;  // the last k with t[k].first_slot <= slot
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    if (L.t[mid].first_slot <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <class PT, class GT, int ROUND>
+__global__ void __launch_bounds__(kStepBlock)
+adamw_sr_inline(const InlineTensors L, uint32_t slot0, Coeffs c, uint32_t seed, uint32_t step) {
+  const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
+  const DevTensor t = L.t[inline_tensor(L, slot)];
+  adamw_slot<PT, GT, ROUND>(t, slot - t.first_slot, c, seed, step);
+}
+
 // Table form, for tensors of any sizes: slot_tensor[s] names the tensor of
 // slot s (filled on the device from the tensors' first slots).
 template <class PT, class GT, int ROUND>
@@ -551,6 +590,14 @@ stream_probe_slots(const DevTensor* __restrict__ tensors, const uint32_t* __rest
   probe_slot<PT, GT>(t, slot - t.first_slot);
 }
 
+template <class PT, class GT>
+__global__ void __launch_bounds__(kStepBlock)
+stream_probe_inline(const InlineTensors L, uint32_t slot0, Coeffs, uint32_t, uint32_t) {
+  const uint32_t slot = slot0 + slot_of_block(blockIdx.x, gridDim.x);
+  const DevTensor t = L.t[inline_tensor(L, slot)];
+  probe_slot<PT, GT>(t, slot - t.first_slot);
+}
+
 // ---------------------------------------------- SR with caller's bits
 // out[i] = SR(x[i], r16[i]): the rounding with its random bits supplied.
 __global__ void __launch_bounds__(kBlock)
@@ -725,9 +772,18 @@ size_t workspace_bound(int32_t n, uint64_t total_slots) {
                   256);
 }
 
+// Table launches of at most this many slots get their slot table from the
+// host, inside the uploaded metadata: that never takes more launches than
+// the device fill (a table of this size adds at most one upload launch and
+// saves the fill launch), and a small step takes two launches instead of
+// three.
+constexpr uint64_t kHostTableSlots = asr::kUploadWords;
+
 struct Launch {
   int group = 0;
   bool by_class = false;
+  bool host_table = false;        // table launches: slot table uploaded with the metadata
+  bool inline_desc = false;       // descriptors in the kernel arguments (adamw_sr_inline)
   std::vector<asr::DevTensor> tensors;
   uint32_t slots_per_tensor = 0;  // size-class launches
   uint64_t n_slots = 0;
@@ -772,6 +828,7 @@ std::string plan_launches(const std::vector<asr::DevTensor> (&group)[asr::kGroup
         }
       }
     }
+    rest.host_table = rest.n_slots <= kHostTableSlots;
     if (!rest.tensors.empty()) out->push_back(std::move(rest));
   }
   return "";
@@ -779,6 +836,7 @@ std::string plan_launches(const std::vector<asr::DevTensor> (&group)[asr::kGroup
 
 using TableKernel = void (*)(const asr::DevTensor*, const uint32_t*, uint32_t, asr::Coeffs,
                              uint32_t, uint32_t);
+using InlineKernel = void (*)(const asr::InlineTensors, uint32_t, asr::Coeffs, uint32_t, uint32_t);
 using ClassKernel = void (*)(const asr::DevTensor*, uint32_t, uint32_t, uint32_t, asr::Coeffs,
                              uint32_t, uint32_t);
 
@@ -804,6 +862,10 @@ template <class PT, class GT, int R>
 struct PickClass {
   static ClassKernel get() { return asr::adamw_sr_class<PT, GT, R>; }
 };
+template <class PT, class GT, int R>
+struct PickInline {
+  static InlineKernel get() { return asr::adamw_sr_inline<PT, GT, R>; }
+};
 // the traffic probe of the same launch (the rounding does not apply)
 template <class PT, class GT, int>
 struct PickProbeTable {
@@ -812,6 +874,10 @@ struct PickProbeTable {
 template <class PT, class GT, int>
 struct PickProbeClass {
   static ClassKernel get() { return asr::stream_probe_class<PT, GT>; }
+};
+template <class PT, class GT, int>
+struct PickProbeInline {
+  static InlineKernel get() { return asr::stream_probe_inline<PT, GT>; }
 };
 
 // LDS reserved per workgroup to hold the step kernel at kBlocksPerCU
@@ -834,6 +900,22 @@ hipError_t run_launch(const Launch& l, uint8_t* ws, bool probe, int rounding,
   const uint32_t n_slots = static_cast<uint32_t>(l.n_slots);
   hipError_t e;
   uint32_t lds = 0;
+  if (l.inline_desc) {
+    asr::InlineTensors L{};
+    std::copy(l.tensors.begin(), l.tensors.end(), L.t);
+    L.n = static_cast<uint32_t>(l.tensors.size());
+    L.per = l.by_class ? l.slots_per_tensor : 0;
+    L.magic = l.by_class ? 0xFFFFFFFFu / l.slots_per_tensor : 0;
+    const InlineKernel k = probe ? pick_kernel<PickProbeInline>(l.group, rounding)
+                                 : pick_kernel<PickInline>(l.group, rounding);
+    if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
+    for (uint32_t slot0 = 0; slot0 < n_slots; slot0 += std::min(n_slots - slot0, asr::kMaxGrid)) {
+      const uint32_t grid = std::min(n_slots - slot0, asr::kMaxGrid);
+      e = launch_lds(k, grid, asr::kStepBlock, lds, stream, L, slot0, c, seed, step);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (l.by_class) {
     const ClassKernel k = probe ? pick_kernel<PickProbeClass>(l.group, rounding)
                                 : pick_kernel<PickClass>(l.group, rounding);
@@ -849,11 +931,13 @@ hipError_t run_launch(const Launch& l, uint8_t* ws, bool probe, int rounding,
     return hipSuccess;
   }
   auto* d_table = reinterpret_cast<uint32_t*>(ws + l.table_off);
-  const uint32_t fill_grid = std::min<uint32_t>((n_slots + asr::kBlock - 1) / asr::kBlock, 4096u);
-  e = launch(asr::fill_slot_table, fill_grid, stream,
-             reinterpret_cast<const uint32_t*>(ws + l.first_off),
-             static_cast<int32_t>(l.tensors.size()), d_table, n_slots);
-  if (e != hipSuccess) return e;
+  if (!l.host_table) {
+    const uint32_t fill_grid = std::min<uint32_t>((n_slots + asr::kBlock - 1) / asr::kBlock, 4096u);
+    e = launch(asr::fill_slot_table, fill_grid, stream,
+               reinterpret_cast<const uint32_t*>(ws + l.first_off),
+               static_cast<int32_t>(l.tensors.size()), d_table, n_slots);
+    if (e != hipSuccess) return e;
+  }
   const TableKernel k = probe ? pick_kernel<PickProbeTable>(l.group, rounding)
                               : pick_kernel<PickTable>(l.group, rounding);
   if ((e = occupancy_lds(reinterpret_cast<const void*>(k), &lds)) != hipSuccess) return e;
@@ -922,15 +1006,27 @@ int make_plan(const asr_tensor* tensors, int32_t n_tensors, StepPlan* plan) {
   plan->bound_bytes = workspace_bound(n_tensors, bound_slots);
   const std::string err = plan_launches(group, &plan->launches);
   if (!err.empty()) return fail(ASR_EINVAL, err);
+  // A plan whose every launch fits the kernel arguments uploads nothing.
+  bool all_inline = true;
+  for (const Launch& l : plan->launches)
+    all_inline = all_inline && l.tensors.size() <= static_cast<size_t>(asr::kInlineTensors);
+  for (Launch& l : plan->launches) l.inline_desc = all_inline;
 
-  // Workspace offsets: uploaded metadata first, device-filled tables after.
+  // Workspace offsets: uploaded metadata first (descriptors; first slots for
+  // a device-filled table, or the host-filled table itself), device-filled
+  // tables after.
   size_t off = 0;
   for (Launch& l : plan->launches) {
+    if (l.inline_desc) continue;
     off = align_up(off, 16);
     l.tensors_off = off;
     off += l.tensors.size() * sizeof(asr::DevTensor);
-    if (!l.by_class) {
-      off = align_up(off, 16);
+    if (l.by_class) continue;
+    off = align_up(off, 16);
+    if (l.host_table) {
+      l.table_off = off;
+      off += l.n_slots * sizeof(uint32_t);
+    } else {
       l.first_off = off;
       off += l.tensors.size() * sizeof(uint32_t);
     }
@@ -938,7 +1034,7 @@ int make_plan(const asr_tensor* tensors, int32_t n_tensors, StepPlan* plan) {
   const size_t meta_bytes = align_up(off, 16);
   off = meta_bytes;
   for (Launch& l : plan->launches) {
-    if (l.by_class) continue;
+    if (l.inline_desc || l.by_class || l.host_table) continue;
     off = align_up(off, 16);
     l.table_off = off;
     off += l.n_slots * sizeof(uint32_t);
@@ -948,12 +1044,23 @@ int make_plan(const asr_tensor* tensors, int32_t n_tensors, StepPlan* plan) {
     return fail(ASR_EWORKSPACE, "internal: workspace plan exceeds its bound");
   plan->image.assign(meta_bytes, 0);
   for (const Launch& l : plan->launches) {
+    if (l.inline_desc) continue;
     std::memcpy(plan->image.data() + l.tensors_off, l.tensors.data(),
                 l.tensors.size() * sizeof(asr::DevTensor));
-    if (!l.by_class)
-      for (size_t k = 0; k < l.tensors.size(); ++k)
+    if (l.by_class) continue;
+    for (size_t k = 0; k < l.tensors.size(); ++k) {
+      if (!l.host_table) {
         std::memcpy(plan->image.data() + l.first_off + k * sizeof(uint32_t),
                     &l.tensors[k].first_slot, sizeof(uint32_t));
+        continue;
+      }
+      // slots first_slot .. first_slot + tensor_slots - 1 belong to tensor k
+      const uint32_t idx = static_cast<uint32_t>(k);
+      const uint64_t end = l.tensors[k].first_slot + tensor_slots(l.tensors[k]);
+      for (uint64_t sl = l.tensors[k].first_slot; sl < end; ++sl)
+        std::memcpy(plan->image.data() + l.table_off + sl * sizeof(uint32_t), &idx,
+                    sizeof(uint32_t));
+    }
   }
   return ASR_OK;
 }

@@ -9,7 +9,8 @@ peak (algorithmic bytes: 22 per element), and the CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload llama3_8b|llama3_8b_rank|shards|convert|gemm|rng|hbm_probe]
+                    [--workload llama3_8b|llama3_8b_rank|shards|convert|gemm|rng|hbm_probe|
+                                bf16_64k|f32_16m]
     python bench.py --copy-probe      # plain copy of known size (counter scaling)
 
 The llama3_8b_rank workload is one data-parallel rank's share of the same
@@ -20,6 +21,10 @@ ends), each with its global base_index.
 The hbm_probe workload measures what HBM gives the step's launch structure
 without the step's arithmetic: read-only, write-only and copy streams, and
 the Llama-3-8B list's own 4-read/3-write traffic timed against the step.
+
+The bf16_64k and f32_16m workloads step one small tensor: 65,536 bf16
+params (cache-resident, launch-bound) and 16,777,216 f32 params (the f32
+size-class launch; timed with the Infinity Cache flushed between steps).
 
 The gemm workload times the bf16 GEMM with the SR epilogue on the gate/up
 projection of one Llama-3-8B MLP over 8,192 tokens (M=8192, N=14336,
@@ -180,6 +185,15 @@ def gemm_traffic_from_profile(m, n, k):
     return d.get("hbm_bytes_per_launch")
 
 
+# A list of at most this many tensors travels in the kernel arguments (the
+# library's inline launches); a longer one is uploaded first.
+INLINE_TENSORS = 48
+KERNEL_UPLOADED = ("upload_words (the descriptors) + adamw_sr_class<BF16,BF16,SR> (one launch per "
+                   "size class) + adamw_sr_slots<BF16,BF16,SR> (the other tensors)")
+KERNEL_INLINE = ("adamw_sr_inline<BF16,BF16,SR> (descriptors in the kernel arguments; one launch "
+                 "per size class and one for the other pieces)")
+
+
 def run_adamw(args, torch, ops, wl):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -263,11 +277,10 @@ def run_adamw(args, torch, ops, wl):
                    "parallelism": "single GPU", **extra},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "adamw_sr_class<BF16,BF16,SR> (one launch per size class) + "
-                               "adamw_sr_slots<BF16,BF16,SR> (small tensors)",
+                     "kernel": KERNEL_UPLOADED if len(state) > INLINE_TENSORS else KERNEL_INLINE,
                      "kernel_ms_avg": kernel_ms, "kernel_ms_median": kernel_ms_median,
                      "timing": "HIP events on the launch stream around each step call: all "
-                               "kernels of one step (metadata upload, slot table, step)",
+                               "kernels of one step",
                      "copy_GBps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
                      "copy_note": "asr_stream_copy, 2 x 8 GiB, a 1:1 copy built like the step "
                                   "(same slots, 128-bit accesses, XCD windows, residency cap)",
@@ -310,6 +323,81 @@ def run_convert(args, torch, ops, wl):
                          "traffic": stream_traffic_from_profile(
                              "cvt_f32_bf16_sr_2pow30_hbm_counters.json", source_hash(), n),
                          "algorithmic_bytes": 6 * n, "kernel_ms_avg": kernel_ms}}
+
+
+MALL_FLUSH_BYTES = 1 << 30   # > the 256 MB Infinity Cache
+
+
+def run_small(args, torch, ops, wl):
+    """One tensor far below the headline's size, stepped back to back:
+    bf16_64k = 65,536 bf16 params and grads (cache-resident, bound by the
+    launch), f32_16m = 16,777,216 f32 params and grads (28 B per element,
+    469.8 MB per step, the f32 size-class launch). The f32 tensor's 256 MiB
+    of params, grads and states fit the 256 MB Infinity Cache, so it is also
+    timed with a 1 GiB read on the stream between steps (outside the
+    events), which leaves the step to DRAM; that is the roofline figure."""
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.workload == "bf16_64k":
+        n, dt, cfg, std_g, bpe = 65536, torch.bfloat16, wl.CFG_SMALL, 1e-3, 22
+    else:
+        n, dt, cfg, std_g, bpe = 16777216, torch.float32, wl.CFG_F32, 1e-2, 28
+    gen = wl.device_generator(dev, cfg, 0)
+    p = wl.device_normal(n, 0.02, gen, dev, dt)
+    g = wl.device_normal(n, std_g, gen, dev, dt)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    ws = ops.make_workspace([n], dev)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, seed=0,
+              rounding="sr", workspace=ws)
+    step = [0]
+
+    def fn():
+        step[0] += 1
+        ops.adamw_step([p], [g], [m], [v], [0], step=step[0], **hp)
+
+    steps = max(args.steps, 100) if n <= 65536 else args.steps
+    for _ in range(max(args.warmup, 5)):
+        fn()
+    wall_s, ev_ms = _time_launches(torch, stream, fn, steps)
+    res_ctx = {"back_to_back_kernel_ms": ev_ms, "back_to_back_wall_ms": wall_s * 1e3}
+    kernel_ms, note = ev_ms, ("back-to-back steps: the tensor's 1.4 MB stay in the caches, "
+                              "so the time is launch and latency, not HBM")
+    if n > 65536:
+        # the flush reads (a write would leave dirty lines that the step
+        # then writes back)
+        scratch = torch.zeros(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+        for k in range(steps):
+            scratch.sum()
+            events[k][0].record(stream)
+            fn()
+            events[k][1].record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = sum(a.elapsed_time(b) for a, b in events) / steps
+        res_ctx["back_to_back_GBps"] = bpe * n / (ev_ms * 1e-3) / 1e9
+        note = ("each step after a 1 GiB read on the stream (outside the events), so its "
+                "inputs come from DRAM; back-to-back steps partly hit the Infinity Cache")
+        del scratch
+    achieved = bpe * n / (kernel_ms * 1e-3) / 1e9
+    name = "bf16 params and grads" if dt == torch.bfloat16 else "f32 params and grads"
+    return {"metric": METRIC, "value": n / (kernel_ms * 1e-3), "unit": "params/s", "n_gpus": 1,
+            "steps": steps, "warmup": max(args.warmup, 5), "ms_per_step": wall_s * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"single_tensor_{n}", "params": n,
+                       "param_dtype": "bf16" if dt == torch.bfloat16 else "f32",
+                       "grad_dtype": "bf16" if dt == torch.bfloat16 else "f32",
+                       "state_dtype": "f32", "rounding": "sr" if dt == torch.bfloat16 else "none",
+                       "algorithmic_bytes_per_param": bpe},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "adamw_sr_inline (one launch, the descriptor in the "
+                                   "kernel arguments; " + name + ")",
+                         "kernel_ms_avg": kernel_ms, "timing_note": note},
+            "context": res_ctx}
 
 
 GEMM_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
@@ -664,7 +752,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["llama3_8b", "llama3_8b_rank", "shards", "convert", "gemm", "rng",
-                             "hbm_probe"])
+                             "hbm_probe", "bf16_64k", "f32_16m"])
     ap.add_argument("--rank", type=int, default=3, help="rank whose share --workload "
                     "llama3_8b_rank times")
     ap.add_argument("--ranks", type=int, default=8)
@@ -714,6 +802,8 @@ def main():
         res = run_rng(args, torch, ops, wl)
     elif args.workload == "hbm_probe":
         res = run_hbm_probe(args, torch, ops, wl)
+    elif args.workload in ("bf16_64k", "f32_16m"):
+        res = run_small(args, torch, ops, wl)
     else:
         res = run_adamw(args, torch, ops, wl)
     if cpu is not None:

@@ -84,7 +84,10 @@ typedef struct asr_tensor {
  * n_tensors <= 0 or tensors is NULL). Only the count of tensors and their
  * numel matter, so the size stays valid across steps of a fixed list. The
  * workspace holds the list's metadata and a table of one 32-bit entry per
- * 1,024-element slot (under 0.4% of the bf16 parameter bytes). */
+ * 1,024-element slot (under 0.4% of the bf16 parameter bytes). A step whose
+ * launches each cover at most 48 tensors (any list of at most 48 tensors)
+ * passes the metadata in its kernel arguments and leaves the workspace
+ * untouched; the workspace is still required. */
 size_t asr_adamw_workspace_bytes(const asr_tensor* tensors, int32_t n_tensors);
 
 /*

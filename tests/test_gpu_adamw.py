@@ -584,6 +584,47 @@ def test_thousands_of_tensors_and_more_size_classes_than_launches():
                            f"tensor {k} (n={d[0].numel()}) window {s}")
 
 
+@pytest.mark.parametrize("pdt,gdt,rounding", [(BF16, BF16, ROUND_SR), (F32, F32, ROUND_SR),
+                                               (BF16, F32, ROUND_RN)])
+def test_descriptors_in_arguments_and_uploaded_agree(pdt, gdt, rounding):
+    """A list of at most 48 tensors travels in the kernel arguments; one
+    more tensor sends the whole list through the uploaded descriptors (and a
+    slot table). 49 tensors, three of them equal and large enough for a
+    size class, the rest of distinct ragged sizes, odd base indices: the
+    first 48 stepped alone and all 49 stepped together give the same bits,
+    and every element matches the oracle."""
+    dev = torch.device("cuda", 0)
+    rng = wl.host_rng(wl.CFG_SMALL, 4849, pdt * 4 + gdt * 2 + rounding)
+    sizes = [700001] * 3 + [int(x) for x in rng.integers(1, 40000, 46)]
+    assert 3 * ((700001 + 1023) // 1024) >= 2048
+    host, bases, base = [], [], 5
+    for n in sizes:
+        host.append((_host_tensor(rng, n, pdt, 0.02), _host_tensor(rng, n, gdt, 1e-3),
+                     wl.normal_f32(rng, n, 1e-4), np.abs(wl.normal_f32(rng, n, 1e-7))))
+        bases.append(base)
+        base += n + 7
+    rd = "sr" if rounding == ROUND_SR else "rn"
+
+    def run(k):
+        d = [(_to_dev(p, pdt), _to_dev(g, gdt), f32_tensor(m), f32_tensor(v))
+             for p, g, m, v in host[:k]]
+        ops.adamw_step([x[0] for x in d], [x[1] for x in d], [x[2] for x in d],
+                       [x[3] for x in d], bases[:k], step=4, seed=33, rounding=rd, **HP)
+        torch.cuda.synchronize()
+        return [(to_host(x[0]), to_host(x[2]), to_host(x[3])) for x in d]
+
+    announce("descriptors in arguments (48) and uploaded (49)", pdt, gdt, rounding)
+    alone, together = run(48), run(49)
+    for k in range(48):
+        for a, b, what in zip(alone[k], together[k], ("param", "m", "v")):
+            assert_bits_equal(a, b, f"tensor {k} {what}: 48 alone vs 49 together")
+    for k, ((p, g, m, v), got) in enumerate(zip(host, together)):
+        want = oracle.step_tensor(p, g, m, v, param_dtype=pdt, grad_dtype=gdt,
+                                  base_index=bases[k], step=4, seed=33, rounding=rounding, **HP)
+        for x, w, what in zip(got, want, ("param", "m", "v")):
+            assert_bits_equal(x, w, f"tensor {k} (n={sizes[k]}) {what}")
+
+
 def test_overlapping_buffers_are_rejected():
     """p, m and v are written in place, so the binding refuses buffers that
     share memory (here: one tensor's exp_avg_sq is a view into another's
