@@ -1,13 +1,15 @@
 """The library's calls under HIP graph capture (torch.cuda.CUDAGraph).
 
 Every entry point is asynchronous on the caller's stream, takes its
-metadata through kernel arguments (the step uploads its tensor table with a
-small kernel whose argument holds it), and calls no allocation or memset,
-so a sequence of calls can be captured once and replayed. One iteration --
-an AdamW-SR step over a two-tensor list (a size class and the table
-launch), the SR conversion, the SR GEMM in its persistent launch, and
-dropout -- is captured, then replayed three times with eager work and
-synchronizations in between. After every replay the state and the outputs
+metadata through kernel arguments (a step of more than 48 tensors uploads
+its tensor table with a small kernel whose argument holds it, and may fill
+a slot table on the device; a shorter list passes the table in the step
+kernels' own arguments), and calls no allocation or memset, so a sequence
+of calls can be captured once and replayed. One iteration -- an AdamW-SR
+step (a size class and a table launch; a two-tensor list, or 53 tensors
+with a device-filled slot table), the SR conversion, the SR GEMM in its
+persistent launch, and dropout -- is captured, then replayed three times
+with eager work and synchronizations in between. After every replay the state and the outputs
 must equal, bit for bit, those of the same iterations run eagerly (the
 replayed step repeats its captured step number, as the eager runs do)."""
 
@@ -28,14 +30,18 @@ def _gpu():
     require_gpu()
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("n_tiny", [0, 50], ids=["inline", "uploaded"])
+def test_graph_replays_match_eager(n_tiny):
     dev = torch.device("cuda", 0)
-    announce("graph capture: inputs")
+    announce("graph capture: inputs", n_tiny)
     gen = wl.device_generator(dev, wl.CFG_SMALL, 41)
-    sizes = [(1 << 21) + 77, 3000]      # 2049 slots (a size class) and a table launch
+    # 2049 slots (a size class) and a table launch; with the tiny tensors,
+    # 53 tensors and a table of 835 slots (filled on the device)
+    sizes = [(1 << 21) + 77, 3000] + ([800_001] + [17 * k + 1 for k in range(n_tiny)]
+                                      if n_tiny else [])
     p0 = [wl.device_normal(n, 0.02, gen, dev, torch.bfloat16) for n in sizes]
     grads = [wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16) for n in sizes]
-    bases = [0, sizes[0]]
+    bases = [int(x) for x in np.cumsum([0] + sizes[:-1])]
     x = wl.device_normal((1 << 20) + 5, 1.0, gen, dev, torch.float32)
     m, n, k = 4100, 4200, 256            # 17 x 17 big tiles: the persistent launch
     a_bits, b_bits = wl.gemm_operands_host(m, n, k, "int", seed=5)
@@ -105,10 +111,12 @@ def test_graph_noalloc_step_replays_match_eager():
     dev = torch.device("cuda", 0)
     announce("graph capture noalloc: inputs")
     gen = wl.device_generator(dev, wl.CFG_SMALL, 43)
-    sizes = [(1 << 21) + 77, 3000, 65537]
+    # 53 tensors: more than travel in the kernel arguments, so the step's
+    # metadata and slot table live in the scratch
+    sizes = [(1 << 21) + 77, 3000, 65537] + [29 * k + 3 for k in range(50)]
     p0 = [wl.device_normal(n, 0.02, gen, dev, torch.bfloat16) for n in sizes]
     grads = [wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16) for n in sizes]
-    bases = [5, 5 + sizes[0], 5 + sizes[0] + sizes[1]]
+    bases = [int(x) for x in np.cumsum([5] + sizes[:-1])]
 
     def fresh():
         return dict(p=[t.clone() for t in p0],

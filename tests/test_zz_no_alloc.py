@@ -1,8 +1,8 @@
 """asr_adamw_step_noalloc, the step for callers that cannot allocate (it
 runs on the library's static scratch instead of a workspace), against
-asr_adamw_step through the C ABI: two calls in a row, the second with a
-smaller list, bit for bit on params, m and v; and a list too large for the
-scratch is rejected before anything is enqueued."""
+asr_adamw_step through the C ABI: calls in a row, the second with a smaller
+list, bit for bit on params, m and v; and a list too large for the scratch
+is rejected before anything is enqueued."""
 
 import numpy as np
 import pytest
@@ -62,25 +62,33 @@ def _run_both(ts, step, rounding):
 
 
 def test_noalloc_matches_step_two_calls_second_smaller():
-    # call 1: a size class (3 x 700,001 elements: 684 slots each, 2,052 in
-    # all), shifted views and a mixed-size rest for the slot table, every
-    # dtype pair; call 2: a smaller list, so stale entries of call 1 remain
-    # in the scratch past what call 2 writes
+    # Lists of more than 48 tensors keep their metadata in the scratch (a
+    # shorter list passes it in the kernel arguments and leaves the scratch
+    # alone). Call 1: a size class (3 x 700,001 elements: 684 slots each,
+    # 2,052 in all), shifted views, a mixed-size rest and 45 tiny tensors,
+    # every dtype pair: 54 tensors; the bf16/bf16 slot table (about 1,030
+    # entries) is filled on the device, the other pairs' tables come from
+    # the host. Call 2: a smaller list of 50 tensors (host-built tables), so
+    # stale entries of call 1 remain in the scratch past what call 2 writes.
+    # Then call 1's list again, and a list short enough to travel in the
+    # kernel arguments.
+    tiny = [(1 + (37 * k) % 1000, torch.bfloat16, torch.bfloat16, k % 4) for k in range(45)]
     first = [(700_001, torch.bfloat16, torch.bfloat16, 0)] * 2 + \
             [(700_001, torch.bfloat16, torch.bfloat16, 3)] + \
             [(n, pdt, gdt, off) for n, pdt, gdt, off in (
                 (1, torch.bfloat16, torch.bfloat16, 0), (4097, torch.float32, torch.float32, 1),
                 (65_537, torch.bfloat16, torch.float32, 2), (300_007, torch.float32, torch.bfloat16, 0),
-                (2_049, torch.bfloat16, torch.bfloat16, 5), (1_000_003, torch.bfloat16, torch.bfloat16, 0))]
-    second = [(5, torch.bfloat16, torch.bfloat16, 0), (3_001, torch.float32, torch.float32, 0),
-              (10_007, torch.bfloat16, torch.bfloat16, 1)]
+                (2_049, torch.bfloat16, torch.bfloat16, 5), (1_000_003, torch.bfloat16, torch.bfloat16, 0))] + tiny
+    short = [(5, torch.bfloat16, torch.bfloat16, 0), (3_001, torch.float32, torch.float32, 0),
+             (10_007, torch.bfloat16, torch.bfloat16, 1)]
+    second = short + [(1 + (53 * k) % 900, torch.bfloat16, torch.bfloat16, k % 3) for k in range(47)]
+    assert len(first) == 54 and len(second) == 50
     for k, (specs, step, rounding) in enumerate(((first, 3, _abi.ASR_ROUND_SR),
-                                                 (second, 4, _abi.ASR_ROUND_RN))):
+                                                 (second, 4, _abi.ASR_ROUND_RN),
+                                                 (first, 5, _abi.ASR_ROUND_SR),
+                                                 (short, 6, _abi.ASR_ROUND_SR))):
         announce("noalloc call", k + 1, len(specs), "tensors")
         _run_both(_make_list(specs, k), step, rounding)
-    # and a repeat of the first list after the smaller one
-    announce("noalloc call 3")
-    _run_both(_make_list(first, 2), 5, _abi.ASR_ROUND_SR)
 
 
 def test_noalloc_rejects_a_list_beyond_the_scratch():
