@@ -102,12 +102,29 @@ __device__ __forceinline__ float unit(uint32_t w) {
 // error over all of those inputs through asr_box_muller_given_words, which
 // runs this function.
 constexpr float kTwoLn2 = 1.38629436111989061883f;  // 2 ln 2, rounded to binary32
+
+// Correctly rounded square root of an x that is +0 or a positive normal
+// number (here x = 2 ln 2 |log2 u1| lies in [0, 34)). v_sqrt_f32 is within
+// one ulp of the root, so the rounded root is y or one of its neighbours;
+// Tuckerman's test picks it: with exact products (fma), the root lies below
+// the midpoint of y- and y when x <= y- * y, and above the midpoint of y and
+// y+ when x > y * y+. Without the range reduction and special cases of the
+// general form, for inputs that need neither.
+__device__ __forceinline__ float sqrt_rn_nonneg_normal(float x) {
+  const float y = __builtin_amdgcn_sqrtf(x);
+  const float below = __uint_as_float(__float_as_uint(y) - 1u);
+  const float above = __uint_as_float(__float_as_uint(y) + 1u);
+  float r = __builtin_fmaf(-below, y, x) <= 0.0f ? below : y;
+  r = __builtin_fmaf(-y, above, x) > 0.0f ? above : r;
+  return r;
+}
+
 __device__ __forceinline__ void box_muller(uint32_t w_even, uint32_t w_odd, float& zc,
                                            float& zs) {
   const float u1 = static_cast<float>((w_even >> 8) + 1u) * kTwoM24;  // (0, 1], exact
   const float u2 = unit(w_odd);
   // log2 u1 <= 0; its magnitude keeps r = +0 at u1 = 1
-  const float r = __builtin_sqrtf(kTwoLn2 * __builtin_fabsf(__builtin_amdgcn_logf(u1)));
+  const float r = sqrt_rn_nonneg_normal(kTwoLn2 * __builtin_fabsf(__builtin_amdgcn_logf(u1)));
   zc = r * __builtin_amdgcn_cosf(u2);
   zs = r * __builtin_amdgcn_sinf(u2);
 }
