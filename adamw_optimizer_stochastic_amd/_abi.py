@@ -44,6 +44,24 @@ class AsrTensor(ctypes.Structure):
     ]
 
 
+# The same layout as a numpy structured dtype, so that a list's descriptors
+# can be filled column by column.
+ASR_TENSOR_DTYPE = None
+
+
+def _tensor_dtype():
+    import numpy as np
+    dt = np.dtype([("param", np.uint64), ("grad", np.uint64), ("exp_avg", np.uint64),
+                   ("exp_avg_sq", np.uint64), ("numel", np.int64), ("base_index", np.uint64),
+                   ("param_dtype", np.int32), ("grad_dtype", np.int32)])
+    assert dt.itemsize == ctypes.sizeof(AsrTensor)
+    for name, _ in AsrTensor._fields_:
+        assert dt.fields[name][1] == getattr(AsrTensor, name).offset, name
+    return dt
+
+
+ASR_TENSOR_DTYPE = _tensor_dtype()
+
 _c = ctypes
 _SIGNATURES = {
     "asr_abi_version": (_c.c_int, []),
@@ -132,6 +150,27 @@ def asr_adamw_workspace_bytes(tensors):
     """tensors: sequence of AsrTensor (or dicts); only numel is read."""
     arr, n = _tensor_array(tensors)
     return int(lib().asr_adamw_workspace_bytes(arr if n else None, n))
+
+
+def _array_pointer(arr):
+    """A numpy ASR_TENSOR_DTYPE array as the asr_tensor pointer argument."""
+    if arr.dtype != ASR_TENSOR_DTYPE or not arr.flags.c_contiguous:
+        raise TypeError("descriptor array must be a C-contiguous ASR_TENSOR_DTYPE array")
+    return arr.ctypes.data_as(ctypes.POINTER(AsrTensor)) if arr.size else None
+
+
+def asr_adamw_workspace_bytes_array(arr):
+    """asr_adamw_workspace_bytes for a numpy ASR_TENSOR_DTYPE array."""
+    return int(lib().asr_adamw_workspace_bytes(_array_pointer(arr), arr.size))
+
+
+def asr_adamw_step_array(arr, lr, beta1, beta2, eps, weight_decay, step, seed, rounding,
+                         workspace, workspace_bytes, stream):
+    """asr_adamw_step for a numpy ASR_TENSOR_DTYPE array of descriptors."""
+    _check(lib().asr_adamw_step(_array_pointer(arr), arr.size, lr, beta1, beta2, eps,
+                                weight_decay, step, seed, rounding, workspace, workspace_bytes,
+                                stream),
+           "asr_adamw_step")
 
 
 def asr_adamw_host_scalars(lr, beta1, beta2, eps, weight_decay, step):

@@ -8,6 +8,7 @@ kernels; there is no CPU path.
 
 import operator
 
+import numpy as np
 import torch
 
 from . import _abi
@@ -78,13 +79,103 @@ def make_workspace(numels, device):
     return torch.empty(max(workspace_bytes(numels), 1), dtype=torch.uint8, device=device)
 
 
+_STEP_NAMES = ("param", "grad", "exp_avg", "exp_avg_sq")
+_SMALL_LIST = 8   # lists up to this long take the plain overlap check (less fixed cost)
+_ELEM_BYTES = {torch.float32: 4, torch.bfloat16: 2}
+
+
+def _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices, device):
+    """Checks the four lists and returns their asr_tensor array (numpy) and
+    the workspace bytes the step needs. Raises TypeError / ValueError."""
+    n = len(params)
+    lists = (params, grads, exp_avgs, exp_avg_sqs)
+    index = device.index
+    for ts, name in zip(lists, _STEP_NAMES):
+        for i, t in enumerate(ts):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name}[{i}] must be a torch.Tensor")
+            if not t.is_cuda:
+                raise ValueError(f"{name}[{i}] must be on a GPU (got {t.device})")
+            if t.get_device() != index:
+                raise ValueError("all tensors must be on one device")
+            if not t.is_contiguous():
+                raise ValueError(f"{name}[{i}] must be contiguous")
+    pdt, gdt = [p.dtype for p in params], [g.dtype for g in grads]
+    for i, (a, b) in enumerate(zip(pdt, gdt)):
+        if a not in _DTYPE_CODE or b not in _DTYPE_CODE:
+            raise TypeError(f"tensor {i}: params and grads must be float32 or bfloat16")
+    for ts in (exp_avgs, exp_avg_sqs):
+        for i, t in enumerate(ts):
+            if t.dtype != torch.float32:
+                raise TypeError(f"tensor {i}: optimizer states must be float32")
+    numels = [p.numel() for p in params]
+    for ts in lists[1:]:
+        for i, (t, k) in enumerate(zip(ts, numels)):
+            if t.numel() != k:
+                raise ValueError(f"tensor {i}: param, grad and states differ in size")
+    arr = np.zeros(n, dtype=_abi.ASR_TENSOR_DTYPE)
+    ptrs = [[t.data_ptr() for t in ts] for ts in lists]
+    for name, col in zip(_STEP_NAMES, ptrs):
+        arr[name] = col
+    arr["numel"] = numels
+    arr["base_index"] = [_u64(f"base_indices[{i}]", b) for i, b in enumerate(base_indices)]
+    arr["param_dtype"] = [_DTYPE_CODE[d] for d in pdt]
+    arr["grad_dtype"] = [_DTYPE_CODE[d] for d in gdt]
+    # p, m and v are written in place, so no buffer may share memory with another
+    if n <= _SMALL_LIST:
+        sizes = [[k * _ELEM_BYTES[d] for k, d in zip(numels, pdt)],
+                 [k * _ELEM_BYTES[d] for k, d in zip(numels, gdt)],
+                 [k * 4 for k in numels], [k * 4 for k in numels]]
+        check_disjoint((a, b, f"{name}[{i}]")
+                       for name, col, sz in zip(_STEP_NAMES, ptrs, sizes)
+                       for i, (a, b) in enumerate(zip(col, sz)))
+    else:
+        num = np.asarray(numels, dtype=np.int64)
+        sizes = [num * np.asarray([_ELEM_BYTES[d] for d in pdt], dtype=np.int64),
+                 num * np.asarray([_ELEM_BYTES[d] for d in gdt], dtype=np.int64), num * 4, num * 4]
+        starts = np.concatenate([np.asarray(c, dtype=np.uint64) for c in ptrs])
+        _check_disjoint_arrays(starts, np.concatenate(sizes).astype(np.uint64),
+                               lambda k: f"{_STEP_NAMES[k // n]}[{k % n}]")
+    need = _abi.asr_adamw_workspace_bytes_array(arr)
+    return arr, need
+
+
+def _check_disjoint_arrays(starts, nbytes, name_of):
+    """check_disjoint over arrays of starts and sizes (uint64); name_of(k)
+    names span k in the error."""
+    live = np.nonzero(nbytes > 0)[0]
+    if live.size < 2:
+        return
+    order = live[np.argsort(starts[live], kind="stable")]
+    ends = starts[order] + nbytes[order]
+    bad = np.nonzero(starts[order[1:]] < ends[:-1])[0]
+    if bad.size:
+        k0, k1 = int(order[bad[0]]), int(order[bad[0] + 1])
+        raise ValueError(f"{name_of(k0)} and {name_of(k1)} share memory; every buffer of the "
+                         "step must be disjoint from the others")
+
+
+def _step_key(params, grads, exp_avgs, exp_avg_sqs, base_indices, device):
+    """What the descriptors of a list depend on: addresses, sizes, dtypes,
+    base indices and the device."""
+    return (device, tuple(p.data_ptr() for p in params), tuple(g.data_ptr() for g in grads),
+            tuple(m.data_ptr() for m in exp_avgs), tuple(v.data_ptr() for v in exp_avg_sqs),
+            tuple(p.numel() for p in params), tuple(p.dtype for p in params),
+            tuple(g.dtype for g in grads), tuple(base_indices))
+
+
 def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1, beta2,
-               eps, weight_decay, step, seed, rounding="sr", workspace=None):
+               eps, weight_decay, step, seed, rounding="sr", workspace=None, cache=None):
     """One fused AdamW step over lists of tensors on one device (in place).
 
     params: f32 or bf16; grads: f32 or bf16, same numel as their param;
     exp_avgs / exp_avg_sqs: f32; base_indices: global position of element 0
     of each tensor. ``rounding`` ("sr" | "rn") applies to bf16 params.
+
+    ``cache``: optional dict kept by the caller across steps of one list.
+    The checked descriptor array is kept in it and reused while every
+    tensor keeps its address, size and dtype and the base indices stay the
+    same (tensors that moved, or any other change, are checked again).
     """
     n = len(params)
     if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == len(base_indices) == n):
@@ -98,35 +189,27 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
     if n == 0:
         return
     device = params[0].device
-    descs = []
-    for i, (p, g, m, v, b) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs, base_indices)):
-        for t, name in ((p, "param"), (g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")):
-            _require_gpu(t, f"{name}[{i}]")
-            if t.device != device:
-                raise ValueError("all tensors must be on one device")
-        if p.dtype not in _DTYPE_CODE or g.dtype not in _DTYPE_CODE:
-            raise TypeError(f"tensor {i}: params and grads must be float32 or bfloat16")
-        if m.dtype != torch.float32 or v.dtype != torch.float32:
-            raise TypeError(f"tensor {i}: optimizer states must be float32")
-        if not (p.numel() == g.numel() == m.numel() == v.numel()):
-            raise ValueError(f"tensor {i}: param, grad and states differ in size")
-        descs.append(_abi.AsrTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
-                                    p.numel(), _u64(f"base_indices[{i}]", b),
-                                    _DTYPE_CODE[p.dtype], _DTYPE_CODE[g.dtype]))
-    # p, m and v are written in place, so no buffer may share memory with another
-    check_disjoint((t.data_ptr(), t.numel() * t.element_size(), f"{name}[{i}]")
-                   for i, ts in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs))
-                   for t, name in zip(ts, ("param", "grad", "exp_avg", "exp_avg_sq")))
-    need = _abi.asr_adamw_workspace_bytes(descs)
+    if device.type != "cuda":
+        raise ValueError(f"param[0] must be on a GPU (got {device})")
+    if cache is not None:
+        key = _step_key(params, grads, exp_avgs, exp_avg_sqs, base_indices, device)
+        if cache.get("key") != key:
+            cache.clear()
+            cache["arr"], cache["need"] = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs,
+                                                            base_indices, device)
+            cache["key"] = key
+        arr, need = cache["arr"], cache["need"]
+    else:
+        arr, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices, device)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     if workspace.device != device or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must be on {device} and hold {need} bytes")
     with torch.cuda.device(device):
-        _abi.asr_adamw_step(descs, float(lr), float(beta1), float(beta2), float(eps),
-                            float(weight_decay), step, seed, ROUNDING_CODE[rounding],
-                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                            _stream(device))
+        _abi.asr_adamw_step_array(arr, float(lr), float(beta1), float(beta2), float(eps),
+                                  float(weight_decay), step, seed, ROUNDING_CODE[rounding],
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(device))
 
 
 def philox_4x32_fill(n_counters, counter_base, seed, step, counter_upper=0, *, out=None,

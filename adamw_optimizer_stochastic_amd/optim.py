@@ -69,6 +69,7 @@ class AdamWSR(torch.optim.Optimizer):
         self._base_index = {}
         self._next_index = 0
         self._workspaces = {}
+        self._desc_cache = {}
         defaults = dict(lr=lr, betas=tuple(betas), eps=eps, weight_decay=weight_decay,
                         rounding=rounding)
         super().__init__(params, defaults)
@@ -117,17 +118,21 @@ class AdamWSR(torch.optim.Optimizer):
                 self.state[p] = {"step": torch.tensor(0, dtype=torch.int64), "exp_avg": m,
                                  "exp_avg_sq": v}
 
-    def _workspace(self, device, numels):
-        """A cached workspace for this device and its current stream. The step
-        kernels read their metadata from the workspace asynchronously, so a
-        workspace is only reused on the stream that last used it (stream
-        order then separates the steps); another stream gets its own."""
-        need = ops.workspace_bytes(numels)
+    def _workspace(self, device, params):
+        """A cached workspace for this device and its current stream, big
+        enough for a step over `params`. The step kernels read their metadata
+        from the workspace asynchronously, so a workspace is only reused on
+        the stream that last used it (stream order then separates the
+        steps); another stream gets its own. The size bound depends only on
+        the number of tensors and their sizes."""
+        sizes = tuple(p.numel() for p in params)
         key = (device, torch.cuda.current_stream(device).cuda_stream)
-        ws = self._workspaces.get(key)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-            self._workspaces[key] = ws
+        ws, known = self._workspaces.get(key, (None, None))
+        if ws is None or known != sizes:
+            need = ops.workspace_bytes(sizes)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+            self._workspaces[key] = (ws, sizes)
         return ws
 
     @torch.no_grad()
@@ -143,27 +148,31 @@ class AdamWSR(torch.optim.Optimizer):
             if not p.is_contiguous() or not p.grad.is_contiguous():
                 raise NotImplementedError("AdamWSR needs contiguous params and grads")
         self._init_states(live)
-        for group in self.param_groups:
+        for gi, group in enumerate(self.param_groups):
             beta1, beta2 = group["betas"]
+            ps_all = [p for p in group["params"] if p.grad is not None]
+            if not ps_all:
+                continue
+            states = [self.state[p] for p in ps_all]
+            counts = [st["step"] for st in states]
+            # every count moves on together (one call, not one per tensor)
+            torch._foreach_add_(counts, 1)
+            ts = [int(t) for t in torch.stack(counts).tolist()]
             batches = {}  # (device, step) -> lists
-            for p in group["params"]:
-                if p.grad is None:
-                    continue
-                state = self.state[p]
-                state["step"] += 1
-                t = int(state["step"].item())
-                key = (p.device, t)
-                b = batches.setdefault(key, ([], [], [], [], []))
+            for p, st, t in zip(ps_all, states, ts):
+                b = batches.setdefault((p.device, t), ([], [], [], [], []))
                 b[0].append(p)
                 b[1].append(p.grad)
-                b[2].append(state["exp_avg"])
-                b[3].append(state["exp_avg_sq"])
+                b[2].append(st["exp_avg"])
+                b[3].append(st["exp_avg_sq"])
                 b[4].append(self._base_index[p])
             for (device, t), (ps, gs, ms, vs, bases) in batches.items():
+                # the checked descriptors are reused while the tensors stay put
+                cache = self._desc_cache.setdefault((gi, device, tuple(map(id, ps))), {})
                 ops.adamw_step(ps, gs, ms, vs, bases, lr=group["lr"], beta1=beta1, beta2=beta2,
                                eps=group["eps"], weight_decay=group["weight_decay"], step=t,
                                seed=self.seed, rounding=group["rounding"],
-                               workspace=self._workspace(device, [p.numel() for p in ps]))
+                               workspace=self._workspace(device, ps), cache=cache)
         return loss
 
     def state_dict(self):

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from adamw_optimizer_stochastic_amd import ops, random as arng
+from adamw_optimizer_stochastic_amd import _abi, ops, random as arng
 
 
 def test_integer_ranges():
@@ -54,3 +54,37 @@ def test_stream_arguments_checked_before_launch():
         ops.gemm_bf16(ab, ab, rounding="sr", base_index=-1)
     with pytest.raises(ValueError, match="base_index"):
         arng._u64(1 << 64)   # the random module's position argument
+
+
+def test_descriptor_dtype_matches_the_c_struct():
+    """The numpy form of asr_tensor that the step's binding fills has the C
+    struct's size and field offsets."""
+    import ctypes
+    dt = _abi.ASR_TENSOR_DTYPE
+    assert dt.itemsize == ctypes.sizeof(_abi.AsrTensor) == 56
+    for name, _ in _abi.AsrTensor._fields_:
+        assert dt.fields[name][1] == getattr(_abi.AsrTensor, name).offset
+
+
+def test_vectorized_overlap_check_agrees_with_the_plain_one():
+    """The step's array form of the overlap check refuses exactly the span
+    sets that check_disjoint refuses (random spans, some empty, some
+    touching, some nested or identical)."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for trial in range(400):
+        k = int(rng.integers(1, 12))
+        starts = rng.integers(0, 200, k).astype(np.uint64) * 8
+        sizes = (rng.integers(0, 6, k) * 8).astype(np.uint64)
+        spans = [(int(a), int(n), f"s{i}") for i, (a, n) in enumerate(zip(starts, sizes))]
+        try:
+            ops.check_disjoint(spans)
+            plain = None
+        except ValueError as e:
+            plain = str(e)
+        try:
+            ops._check_disjoint_arrays(starts, sizes, lambda i: f"s{i}")
+            arr = None
+        except ValueError as e:
+            arr = str(e)
+        assert (plain is None) == (arr is None), (spans, plain, arr)

@@ -375,6 +375,91 @@ def test_optimizer_class_matches_oracle_and_resumes():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_optimizer_descriptor_cache_follows_moved_tensors():
+    """AdamWSR keeps a list's checked descriptors between steps. Grads that
+    move to new memory, and a parameter whose storage is replaced, must be
+    seen: every step against the oracle bit for bit, with the old memory
+    kept alive so that nothing can land at its former address."""
+    announce("AdamWSR descriptor cache")
+    dev = torch.device("cuda", 0)
+    rng = wl.host_rng(wl.CFG_SMALL, 2718, 0)
+    sizes = [5000, 130, 70001]
+    host_p = [_host_tensor(rng, n, BF16, 0.02) for n in sizes]
+    params = [torch.nn.Parameter(bf16_tensor(h)) for h in host_p]
+    opt = AdamWSR(params, lr=1e-3, weight_decay=0.01, seed=8)
+    host = [[h, np.zeros(n, np.float32), np.zeros(n, np.float32)] for h, n in zip(host_p, sizes)]
+    bases = np.cumsum([0] + sizes)[:-1]
+    keep = []
+    for it in range(4):
+        gh = [_host_tensor(rng, n, BF16, 1e-3) for n in sizes]
+        if it in (0, 1):      # the same grad tensors refilled: a cache hit in step 2
+            if it == 0:
+                for p, g in zip(params, gh):
+                    p.grad = bf16_tensor(g)
+            else:
+                for p, g in zip(params, gh):
+                    p.grad.copy_(bf16_tensor(g))
+        else:                 # fresh grads at new addresses
+            keep += [p.grad for p in params]
+            for p, g in zip(params, gh):
+                p.grad = bf16_tensor(g)
+        if it == 3:           # a parameter moves to new storage
+            keep.append(params[2].data)
+            params[2].data = params[2].data.clone()
+        opt.step()
+        for k, h in enumerate(host):
+            h[0], h[1], h[2] = oracle.step_tensor(h[0], gh[k], h[1], h[2], param_dtype=BF16,
+                                                  grad_dtype=BF16, base_index=int(bases[k]),
+                                                  step=it + 1, seed=8, **HP)
+            what = f"step {it + 1} tensor {k}"
+            assert_bits_equal(wl.tensor_to_bf16_bits(params[k].detach()), h[0], what + " param")
+            assert_bits_equal(to_host(opt.state[params[k]]["exp_avg"]), h[1], what + " m")
+            assert_bits_equal(to_host(opt.state[params[k]]["exp_avg_sq"]), h[2], what + " v")
+    assert all(int(opt.state[p]["step"]) == 4 for p in params)
+    del keep
+
+
+def test_step_cache_reuses_and_rechecks():
+    """ops.adamw_step with a cache: the second call over the same tensors
+    reuses the checked descriptors; a list whose tensor moved is checked
+    again (here: an overlap that only the new list has is refused)."""
+    announce("step cache")
+    dev = torch.device("cuda", 0)
+    gen = wl.device_generator(dev, wl.CFG_SMALL, 31)
+    sizes = [4099, 77, 1 << 16]
+    mk = lambda: ([wl.device_normal(n, 0.02, gen, dev, torch.bfloat16) for n in sizes],
+                  [wl.device_normal(n, 1e-3, gen, dev, torch.bfloat16) for n in sizes],
+                  [torch.zeros(n, dtype=torch.float32, device=dev) for n in sizes],
+                  [torch.zeros(n, dtype=torch.float32, device=dev) for n in sizes])
+    p, g, m, v = mk()
+    ref = ([t.clone() for t in p], g, [t.clone() for t in m], [t.clone() for t in v])
+    bases = [0, 4099, 4176]
+    cache = {}
+    for t in (1, 2):
+        ops.adamw_step(p, g, m, v, bases, step=t, seed=2, cache=cache, **HP)
+        arr = cache["arr"]
+        ops.adamw_step(*ref, bases, step=t, seed=2, **HP)
+    assert cache["arr"] is arr
+    for a, b in zip(p + m + v, ref[0] + ref[2] + ref[3]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+    bad_v = list(v)
+    bad_v[1] = m[2][:77]                         # exp_avg_sq[1] inside exp_avg[2]
+    with pytest.raises(ValueError, match=r"(exp_avg\[2\] and exp_avg_sq\[1\]|"
+                                         r"exp_avg_sq\[1\] and exp_avg\[2\]) share memory"):
+        ops.adamw_step(p, g, m, bad_v, bases, step=3, seed=2, cache=cache, **HP)
+    # a longer list (the array form of the overlap check): grad[10] lies in param[11]
+    n = 12
+    ps = [torch.zeros(100 + k, dtype=torch.bfloat16, device=dev) for k in range(n)]
+    gs = [torch.zeros_like(t) for t in ps]
+    ms = [torch.zeros(t.numel(), dtype=torch.float32, device=dev) for t in ps]
+    vs = [torch.zeros(t.numel(), dtype=torch.float32, device=dev) for t in ps]
+    gs[10] = ps[11][1:111]
+    with pytest.raises(ValueError,
+                       match=r"grad\[10\] and param\[11\]|param\[11\] and grad\[10\]"):
+        ops.adamw_step(ps, gs, ms, vs, list(range(0, 1200, 100)), step=1, seed=2, **HP)
+
+
 def test_optimizer_param_groups_dtypes_and_roundings():
     """AdamWSR with three groups -- bf16 params under SR, an f32 param, a bf16
     param under RN -- each with its own lr and weight decay, one param that
