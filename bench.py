@@ -555,33 +555,50 @@ def run_gemm(args, torch, ops, wl):
     def lib():
         torch.matmul(a, b.t(), out=c)
 
+    # the unfused alternative: the vendor library's GEMM to f32, then the
+    # library's SR conversion of it (the same keying: position m*N + n)
+    c32 = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+    def lib_then_sr():
+        step[0] += 1
+        torch.mm(a, b.t(), out_dtype=torch.float32, out=c32)
+        ops.cvt_f32_bf16_sr(c32, 7, step[0], 0, out=c)
+
+    try:
+        lib_then_sr()
+    except (RuntimeError, TypeError):   # no f32-output GEMM in this torch build
+        lib_then_sr = None
+
     # clocks settle after a fraction of a second of matrix work: warm up on
     # the GEMM itself before any timed loop
     for _ in range(max(100, args.warmup)):
         sr()
-    for fn in (sr, rn, lib):
-        for _ in range(args.warmup):
+    for fn in (sr, rn, lib, lib_then_sr):
+        for _ in range(args.warmup if fn else 0):
             fn()
     # SR and RN timed in alternating blocks, so that clock drift during the
     # run does not favour whichever is timed later
-    walls, srs, rns, libs = [], [], [], []
+    walls, srs, rns, libs, unfused = [], [], [], [], []
     for _ in range(3):
         w, k_ms = _time_launches(torch, stream, sr, args.steps)
         walls.append(w)
         srs.append(k_ms)
         rns.append(_time_launches(torch, stream, rn, args.steps)[1])
         libs.append(_time_launches(torch, stream, lib, args.steps)[1])
+        if lib_then_sr:
+            unfused.append(_time_launches(torch, stream, lib_then_sr, args.steps)[1])
     wall = sum(walls) / len(walls)
     kernel_ms = sum(srs) / len(srs)
     rn_ms = sum(rns) / len(rns)
     lib_ms = sum(libs) / len(libs)
+    unfused_ms = sum(unfused) / len(unfused) if unfused else None
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     return {
         "metric": "bf16 GEMM with stochastic-rounding epilogue, TFLOP/s, 1 GPU",
         "value": flops / wall / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
-        "timing_note": "3 alternating blocks of `steps` launches each of SR, RN and torch.matmul; "
-                       "value and ms_per_step from the SR blocks",
+        "timing_note": "3 alternating blocks of `steps` launches each of SR, RN, torch.matmul "
+                       "and the unfused SR; value and ms_per_step from the SR blocks",
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "m": m, "n": n, "k": k, "layout": "C = A B^T",
                    "rounding": "sr", "accumulate": "f32"},
@@ -595,7 +612,11 @@ def run_gemm(args, torch, ops, wl):
                     "same_kernel_rn_tflops": flops / (rn_ms * 1e-3) / 1e12,
                     "torch_matmul_rn_ms": lib_ms,
                     "torch_matmul_rn_tflops": flops / (lib_ms * 1e-3) / 1e12,
-                    "sr_over_rn": kernel_ms / rn_ms},
+                    "sr_over_rn": kernel_ms / rn_ms,
+                    "unfused_sr_ms": unfused_ms,
+                    "unfused_sr_tflops": flops / (unfused_ms * 1e-3) / 1e12 if unfused_ms else None,
+                    "unfused_note": "torch.mm to f32 (the vendor library) then asr_cvt_f32_bf16_sr "
+                                    "of the f32 product: the same SR keying, without fusion"},
     }
 
 
