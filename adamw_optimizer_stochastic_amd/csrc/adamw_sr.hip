@@ -19,11 +19,13 @@
 // f32, 64-bit for bf16), Philox in registers with one call per 4 consecutive
 // positions (no generator state in memory), no LDS and no matrix cores.
 // Every workgroup takes one slot of 1,024 elements and exits (no loop); the
-// slots of a launch are spread over eight address windows, one per XCD, and
-// a residency cap (LDS reservation) keeps about 24 KiB in flight per CU.
-// Tensors of equal size share a launch and find their tensor by a
-// multiply-high division of the slot index; the rest use a slot-to-tensor
-// table filled on the device, so one call covers thousands of tensors.
+// slots of a launch are spread over four address windows (XCDs x and x + 4
+// share window x), and a residency cap (LDS reservation) keeps about 24 KiB
+// in flight per CU. Tensors of equal size share a launch and find their
+// tensor by a multiply-high division of the slot index; the rest use a
+// slot-to-tensor table (built on the host when small, else filled on the
+// device), so one call covers thousands of tensors. A list of at most 48
+// tensors per launch passes its descriptors in the kernel arguments.
 #include "device.hpp"
 #include "status.hpp"
 
@@ -759,10 +761,12 @@ constexpr uint64_t kClassMinSlots = 2048;
 constexpr int kMaxClassLaunches = 64;
 constexpr int kMaxLaunches = asr::kGroups * (kMaxClassLaunches + 1);
 
-// Workspace layout: first every launch's DevTensor array and (table
-// launches) its first_slot array, each 16-byte aligned (this prefix is
-// uploaded from the host); then every table launch's slot table, filled on
-// the device. The bound covers any split of the tensors into launches.
+// Workspace layout: first every launch's DevTensor array and, for a table
+// launch, its slot table when the host builds it (at most kHostTableSlots
+// entries) or else its first_slot array, each 16-byte aligned (this prefix
+// is uploaded from the host); then the slot tables filled on the device.
+// A plan whose launches all take their descriptors in the kernel arguments
+// uses none of it. The bound covers any split of the tensors into launches.
 size_t workspace_bound(int32_t n, uint64_t total_slots) {
   if (n <= 0) return 0;
   const size_t pad = 3 * 16 * static_cast<size_t>(kMaxLaunches);
