@@ -165,17 +165,19 @@ def _step_key(params, grads, exp_avgs, exp_avg_sqs, base_indices, device):
 
 
 def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1, beta2,
-               eps, weight_decay, step, seed, rounding="sr", workspace=None, cache=None):
+               eps, weight_decay, step, seed, rounding="sr", workspace=None, _cache=None):
     """One fused AdamW step over lists of tensors on one device (in place).
 
     params: f32 or bf16; grads: f32 or bf16, same numel as their param;
     exp_avgs / exp_avg_sqs: f32; base_indices: global position of element 0
     of each tensor. ``rounding`` ("sr" | "rn") applies to bf16 params.
 
-    ``cache``: optional dict kept by the caller across steps of one list.
-    The checked descriptor array is kept in it and reused while every
+    ``_cache`` (internal, for AdamWSR): a dict kept across steps of one
+    list. The checked descriptor array is kept in it and reused while every
     tensor keeps its address, size and dtype and the base indices stay the
-    same (tensors that moved, or any other change, are checked again).
+    same; anything else is checked again. Contiguity and the device are
+    checked only then, so the caller must keep its tensors contiguous and on
+    one device (AdamWSR checks its parameters and grads at every step).
     """
     n = len(params)
     if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == len(base_indices) == n):
@@ -188,17 +190,24 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
         raise ValueError("step must be in [1, 2**32 - 1]")
     if n == 0:
         return
+    if not isinstance(params[0], torch.Tensor):
+        raise TypeError("param[0] must be a torch.Tensor")
     device = params[0].device
     if device.type != "cuda":
         raise ValueError(f"param[0] must be on a GPU (got {device})")
-    if cache is not None:
-        key = _step_key(params, grads, exp_avgs, exp_avg_sqs, base_indices, device)
-        if cache.get("key") != key:
-            cache.clear()
-            cache["arr"], cache["need"] = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs,
-                                                            base_indices, device)
-            cache["key"] = key
-        arr, need = cache["arr"], cache["need"]
+    if _cache is not None:
+        try:
+            key = _step_key(params, grads, exp_avgs, exp_avg_sqs, base_indices, device)
+        except (AttributeError, TypeError):   # not all tensors: the full check says why
+            key = None
+        if key is None or _cache.get("key") != key:
+            _cache.clear()
+            arr, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices,
+                                          device)
+            if key is not None:
+                _cache.update(key=key, arr=arr, need=need)
+        else:
+            arr, need = _cache["arr"], _cache["need"]
     else:
         arr, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices, device)
     if workspace is None:

@@ -172,7 +172,7 @@ class AdamWSR(torch.optim.Optimizer):
                 ops.adamw_step(ps, gs, ms, vs, bases, lr=group["lr"], beta1=beta1, beta2=beta2,
                                eps=group["eps"], weight_decay=group["weight_decay"], step=t,
                                seed=self.seed, rounding=group["rounding"],
-                               workspace=self._workspace(device, ps), cache=cache)
+                               workspace=self._workspace(device, ps), _cache=cache)
         return loss
 
     def state_dict(self):

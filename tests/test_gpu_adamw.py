@@ -420,9 +420,10 @@ def test_optimizer_descriptor_cache_follows_moved_tensors():
 
 
 def test_step_cache_reuses_and_rechecks():
-    """ops.adamw_step with a cache: the second call over the same tensors
-    reuses the checked descriptors; a list whose tensor moved is checked
-    again (here: an overlap that only the new list has is refused)."""
+    """ops.adamw_step with the descriptor cache AdamWSR passes: the second
+    call over the same tensors reuses the checked descriptors; a list whose
+    tensor moved is checked again (here: an overlap that only the new list
+    has is refused)."""
     announce("step cache")
     dev = torch.device("cuda", 0)
     gen = wl.device_generator(dev, wl.CFG_SMALL, 31)
@@ -436,7 +437,7 @@ def test_step_cache_reuses_and_rechecks():
     bases = [0, 4099, 4176]
     cache = {}
     for t in (1, 2):
-        ops.adamw_step(p, g, m, v, bases, step=t, seed=2, cache=cache, **HP)
+        ops.adamw_step(p, g, m, v, bases, step=t, seed=2, _cache=cache, **HP)
         arr = cache["arr"]
         ops.adamw_step(*ref, bases, step=t, seed=2, **HP)
     assert cache["arr"] is arr
@@ -447,7 +448,7 @@ def test_step_cache_reuses_and_rechecks():
     bad_v[1] = m[2][:77]                         # exp_avg_sq[1] inside exp_avg[2]
     with pytest.raises(ValueError, match=r"(exp_avg\[2\] and exp_avg_sq\[1\]|"
                                          r"exp_avg_sq\[1\] and exp_avg\[2\]) share memory"):
-        ops.adamw_step(p, g, m, bad_v, bases, step=3, seed=2, cache=cache, **HP)
+        ops.adamw_step(p, g, m, bad_v, bases, step=3, seed=2, _cache=cache, **HP)
     # a longer list (the array form of the overlap check): grad[10] lies in param[11]
     n = 12
     ps = [torch.zeros(100 + k, dtype=torch.bfloat16, device=dev) for k in range(n)]
