@@ -121,8 +121,19 @@ def lib():
                     fn.argtypes = args
                 if handle.asr_abi_version() != ABI_VERSION:
                     raise RuntimeError("libadamw_sr.so ABI version mismatch; rebuild it")
+                # the step's entry points once more, taking the descriptor
+                # array as a plain address (a numpy array's buffer)
+                for name in ("asr_adamw_workspace_bytes", "asr_adamw_step"):
+                    res, args = _SIGNATURES[name]
+                    fn = handle[name]   # a separate function object for the same symbol
+                    fn.restype = res
+                    fn.argtypes = [_c.c_void_p] + args[1:]
+                    _by_address[name] = fn
                 _lib = handle
     return _lib
+
+
+_by_address = {}
 
 
 def _check(status, func):
@@ -152,24 +163,27 @@ def asr_adamw_workspace_bytes(tensors):
     return int(lib().asr_adamw_workspace_bytes(arr if n else None, n))
 
 
-def _array_pointer(arr):
-    """A numpy ASR_TENSOR_DTYPE array as the asr_tensor pointer argument."""
+def array_address(arr):
+    """The address of a numpy ASR_TENSOR_DTYPE array's descriptors, for the
+    *_at entry points (None for an empty array). The array must stay alive
+    while the address is used."""
     if arr.dtype != ASR_TENSOR_DTYPE or not arr.flags.c_contiguous:
         raise TypeError("descriptor array must be a C-contiguous ASR_TENSOR_DTYPE array")
-    return arr.ctypes.data_as(ctypes.POINTER(AsrTensor)) if arr.size else None
+    return arr.ctypes.data if arr.size else None
 
 
-def asr_adamw_workspace_bytes_array(arr):
-    """asr_adamw_workspace_bytes for a numpy ASR_TENSOR_DTYPE array."""
-    return int(lib().asr_adamw_workspace_bytes(_array_pointer(arr), arr.size))
+def asr_adamw_workspace_bytes_at(address, n):
+    """asr_adamw_workspace_bytes for n descriptors at `address` (array_address)."""
+    lib()
+    return int(_by_address["asr_adamw_workspace_bytes"](address, n))
 
 
-def asr_adamw_step_array(arr, lr, beta1, beta2, eps, weight_decay, step, seed, rounding,
-                         workspace, workspace_bytes, stream):
-    """asr_adamw_step for a numpy ASR_TENSOR_DTYPE array of descriptors."""
-    _check(lib().asr_adamw_step(_array_pointer(arr), arr.size, lr, beta1, beta2, eps,
-                                weight_decay, step, seed, rounding, workspace, workspace_bytes,
-                                stream),
+def asr_adamw_step_at(address, n, lr, beta1, beta2, eps, weight_decay, step, seed, rounding,
+                      workspace, workspace_bytes, stream):
+    """asr_adamw_step for n descriptors at `address` (array_address)."""
+    lib()
+    _check(_by_address["asr_adamw_step"](address, n, lr, beta1, beta2, eps, weight_decay, step,
+                                         seed, rounding, workspace, workspace_bytes, stream),
            "asr_adamw_step")
 
 

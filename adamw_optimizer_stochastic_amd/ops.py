@@ -85,8 +85,9 @@ _ELEM_BYTES = {torch.float32: 4, torch.bfloat16: 2}
 
 
 def _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices, device):
-    """Checks the four lists and returns their asr_tensor array (numpy) and
-    the workspace bytes the step needs. Raises TypeError / ValueError."""
+    """Checks the four lists and returns their asr_tensor array (numpy), its
+    address and the workspace bytes the step needs. Raises TypeError /
+    ValueError."""
     n = len(params)
     lists = (params, grads, exp_avgs, exp_avg_sqs)
     index = device.index
@@ -136,8 +137,8 @@ def _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices, device
         starts = np.concatenate([np.asarray(c, dtype=np.uint64) for c in ptrs])
         _check_disjoint_arrays(starts, np.concatenate(sizes).astype(np.uint64),
                                lambda k: f"{_STEP_NAMES[k // n]}[{k % n}]")
-    need = _abi.asr_adamw_workspace_bytes_array(arr)
-    return arr, need
+    address = _abi.array_address(arr)
+    return arr, address, _abi.asr_adamw_workspace_bytes_at(address, n)
 
 
 def _check_disjoint_arrays(starts, nbytes, name_of):
@@ -202,23 +203,24 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, base_indices, *, lr, beta1,
             key = None
         if key is None or _cache.get("key") != key:
             _cache.clear()
-            arr, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices,
-                                          device)
-            if key is not None:
-                _cache.update(key=key, arr=arr, need=need)
+            arr, address, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs,
+                                                   base_indices, device)
+            if key is not None:   # (the array stays alive in the cache with its address)
+                _cache.update(key=key, arr=arr, address=address, need=need)
         else:
-            arr, need = _cache["arr"], _cache["need"]
+            arr, address, need = _cache["arr"], _cache["address"], _cache["need"]
     else:
-        arr, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs, base_indices, device)
+        arr, address, need = _step_descriptors(params, grads, exp_avgs, exp_avg_sqs,
+                                               base_indices, device)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     if workspace.device != device or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must be on {device} and hold {need} bytes")
     with torch.cuda.device(device):
-        _abi.asr_adamw_step_array(arr, float(lr), float(beta1), float(beta2), float(eps),
-                                  float(weight_decay), step, seed, ROUNDING_CODE[rounding],
-                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                  _stream(device))
+        _abi.asr_adamw_step_at(address, n, float(lr), float(beta1), float(beta2), float(eps),
+                               float(weight_decay), step, seed, ROUNDING_CODE[rounding],
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(device))
 
 
 def philox_4x32_fill(n_counters, counter_base, seed, step, counter_upper=0, *, out=None,

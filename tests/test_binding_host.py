@@ -88,3 +88,15 @@ def test_vectorized_overlap_check_agrees_with_the_plain_one():
         except ValueError as e:
             arr = str(e)
         assert (plain is None) == (arr is None), (spans, plain, arr)
+
+
+def test_descriptor_address_checks_the_array():
+    """Only a C-contiguous array of the descriptor dtype is passed by address."""
+    import numpy as np
+    assert _abi.array_address(np.zeros(0, dtype=_abi.ASR_TENSOR_DTYPE)) is None
+    a = np.zeros(3, dtype=_abi.ASR_TENSOR_DTYPE)
+    assert _abi.array_address(a) == a.ctypes.data
+    with pytest.raises(TypeError):
+        _abi.array_address(np.zeros(3, dtype=np.uint64))
+    with pytest.raises(TypeError):
+        _abi.array_address(a[::2])
